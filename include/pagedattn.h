@@ -1,0 +1,168 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged KV attention library.
+ *
+ * The library computes causal scaled-dot-product attention of a step's new
+ * query tokens over a block-paged KV cache with grouped-query heads, for a
+ * flattened ragged batch that may mix decode tokens, short verification
+ * blocks and prefill chunks (page "32. Production attention kernels", One
+ * kernel for the whole batch; page "Attention kernels", One kernel family,
+ * three uses).  It also writes new K/V rows into the pools through a slot map.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All buffers are device memory owned by the caller.  The library
+ *   allocates nothing per call, keeps no per-call state and never reads
+ *   device memory back in paged_attention / kv_cache_write, so both can be
+ *   captured in a hipGraph; the only cached state is the CU count per device.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *   void*; NULL = the default stream).  Nothing is synchronised.
+ * - Element types: PA_F32 or PA_BF16 for q, out, pools and new rows.  All
+ *   metadata is int32.
+ * - Strides are in elements.  The head dimension must be contiguous.
+ * - On any error nothing is launched and no output is touched.  Device
+ *   data (lengths, page ids, slots) is not validated on the hot path: kernels
+ *   clamp lengths to the table, and pa_validate() checks the data on request.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,          /* a required pointer is NULL                        */
+  PA_ERR_SHAPE = 2,         /* sizes/strides inconsistent (Hq % Hkv, D stride..)  */
+  PA_ERR_UNSUPPORTED = 3,   /* dtype, head_dim or page_size not built            */
+  PA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required       */
+  PA_ERR_LAUNCH = 5,        /* the HIP runtime refused a launch                  */
+  PA_ERR_INVALID_DATA = 6   /* pa_validate only: device metadata out of range   */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/*
+ * Host-side description of one call.  Only host scalars live here; every
+ * per-step quantity (lengths, positions, page ids) is read from device
+ * buffers, so a launch captured in a graph stays valid as sequences grow
+ * (page "Attention kernels", Walking the block table).
+ */
+typedef struct pa_dims {
+  int32_t num_seqs;        /* B: sequences in the flattened batch                 */
+  int32_t num_tokens;      /* N: query tokens (rows of q and out)                  */
+  int32_t max_query_len;   /* host upper bound on any sequence's tokens; 0 = N     */
+  int32_t num_q_heads;     /* Hq                                                   */
+  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0, group G = Hq / Hkv               */
+  int32_t head_dim;        /* D in {64, 128, 256}                                  */
+  int32_t page_size;       /* ps in {16, 32, 64, 128}                              */
+  int32_t num_pages;       /* P: pages in each pool                                */
+  int32_t table_width;     /* W: entries per block-table row                       */
+  int32_t num_splits;      /* split-KV count for decode rows; 0 = automatic        */
+  int64_t q_stride_tok;    /* q  [N, Hq, D]: element stride between tokens         */
+  int64_t q_stride_head;   /*                element stride between heads          */
+  int64_t o_stride_tok;    /* out[N, Hq, D]                                        */
+  int64_t o_stride_head;
+  int64_t kv_stride_page;  /* pools: element strides of page, slot and head;       */
+  int64_t kv_stride_slot;  /* the default layout [P, ps, Hkv, D] has               */
+  int64_t kv_stride_head;  /* (ps*Hkv*D, Hkv*D, D).  K and V share the strides.    */
+} pa_dims;
+
+/*
+ * paged_attention -- out = attention(q, K, V) for every query row.
+ *
+ * Definition (page "32. Production attention kernels", One kernel for the
+ * whole batch and its first point; page "Attention and KV Cache", Attention as
+ * primitive ops; page "paged-attn-xpu", Validation):
+ *   sequence b owns flat rows [qsl[b], qsl[b+1]) with n = qsl[b+1]-qsl[b];
+ *   L = clamp(context_lens[b], 0, W*ps) counts every cached position
+ *   including the step's own tokens; token t sits at pos = L - n + t;
+ *   query head h reads KV head h / G; key j (0 <= j < L) is stored at page
+ *   block_tables[b*W + j/ps], slot j%ps; it is visible to token t iff
+ *   causal == 0 or j <= pos;  out = softmax(scale * q.K^T over visible keys) V,
+ *   and a row with no visible key is exactly zero.
+ *
+ * Arguments
+ *   q             [N, Hq, D] (strides in dims), element type `dtype`.
+ *   k_pool/v_pool [P, ps, Hkv, D] by the strides in dims.
+ *   block_tables  int32 [B, W], row-major; entries past a sequence's
+ *                 ceil(L/ps) pages are never read.
+ *   context_lens  int32 [B].
+ *   query_start_loc int32 [B+1], qsl[0] = 0, non-decreasing, qsl[B] = N.
+ *   scale         finite float; scores are scale * q.k.
+ *   causal        nonzero applies the position rule above.
+ *   out           [N, Hq, D], same element type as q.  Rows not covered by
+ *                 [qsl[0], qsl[B]) are not written.
+ *   workspace     device scratch of at least pa_workspace_size(dims, dtype)
+ *                 bytes (may be NULL when that size is 0).  Needs no
+ *                 initialisation; contents are undefined afterwards.
+ * Returns PA_OK, or an error status with nothing launched.
+ */
+pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start_loc, float scale, int causal,
+                          void* out, void* workspace, size_t workspace_bytes,
+                          const pa_dims* dims, pa_dtype dtype, void* stream);
+
+/*
+ * kv_cache_write -- scatter new K/V rows into the pools.
+ *
+ * Token i's rows k_new[i, :, :] and v_new[i, :, :] ([num_tokens, Hkv, D] with
+ * the given token and head strides, D contiguous) go to flat slot
+ * s = slot_mapping[i] = page * ps + offset of both pools; s < 0 writes
+ * nothing (page "Attention and KV Cache", Paged KV: the write map; page
+ * "32. Production attention kernels", write through slot_mapping).  Slots
+ * >= P*ps are skipped as a guard; duplicate slots are a caller error that
+ * only pa_validate reports.  Uses dims->num_kv_heads, head_dim, page_size,
+ * num_pages and the kv strides.
+ */
+pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                         const int32_t* slot_mapping, int32_t num_tokens,
+                         int64_t new_stride_tok, int64_t new_stride_head,
+                         const pa_dims* dims, pa_dtype dtype, void* stream);
+
+/*
+ * pa_workspace_size -- bytes of workspace paged_attention needs for these
+ * dims: num_splits * (rows) * (D + 2) * 4 when split-KV partials are used
+ * (float32 accumulator, running max and sum per split; page "Attention
+ * kernels", Decode: GQA packing and split-KV), else 0.  Returns 0 for
+ * invalid dims as well; paged_attention reports those.
+ */
+size_t pa_workspace_size(const pa_dims* dims, pa_dtype dtype);
+
+/*
+ * pa_choose_splits -- the split count paged_attention will use for these
+ * dims: dims->num_splits when > 0, else enough workgroups to fill every CU of
+ * the current device with a minimum number of pages per split (page "32.
+ * Production attention kernels", How many splits?).  Returns 1 for invalid dims.
+ */
+int32_t pa_choose_splits(const pa_dims* dims);
+
+/*
+ * pa_validate -- SYNCHRONOUS debug/test check of device metadata.
+ * Copies the metadata to the host and checks: 0 <= qsl[b] <= qsl[b+1],
+ * qsl[0] == 0, qsl[B] == N; 0 <= context_lens[b] <= W*ps; n <= L when
+ * causal (a token with pos < 0 sees nothing); every block-table entry a
+ * sequence uses lies in [0, P); and, when slot_mapping is not NULL, every
+ * slot is -1 or in [0, P*ps) and no slot repeats (page "Attention and KV
+ * Cache": a checked write map refuses a slot outside the pool or named
+ * twice).  Returns PA_OK, PA_ERR_INVALID_DATA, or an argument error.
+ */
+pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* query_start_loc, const int32_t* slot_mapping,
+                      int32_t num_slots, int causal, const pa_dims* dims, void* stream);
+
+/* pa_status_string -- static human-readable text for a status code. */
+const char* pa_status_string(pa_status status);
+
+/* pa_device_cu_count -- compute units of the current device (cached). */
+int32_t pa_device_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,28 @@
+"""CPU float64 oracle for paged KV attention -- TEST INFRASTRUCTURE ONLY.
+
+Nothing in the product path may import, call or link this package.  Only the
+tests (``tests/``), ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the HIP library: it reads the same
+seeded inputs (``workloads``) and computes the plain definition of causal
+grouped-query attention over a block-paged cache, in float64.
+
+Functions (each cites the passage it follows in ``oracle/attention.py``):
+
+* ``attention_f64``     -- gather each sequence's pages, then dense softmax
+                           attention in float64 (the gather-then-dense reference
+                           of page "paged-attn-xpu" and of the reference backend of
+                           page "32. Production attention kernels").
+* ``brute_force``       -- pure-Python scalar loops with ``math.exp`` and
+                           ``math.fsum``; every pool address is computed from
+                           strides.  Tiny inputs only.
+* ``split_combine_f64`` -- split-KV: per-split normalised output and
+                           log-sum-exp, merged with weights exp(lse_s - lse).
+* ``kv_write_ref``      -- the slot-mapped scatter of new K/V rows into the pools.
+
+All three attention functions are pinned against brute force, a library special
+case, closed forms and invariants in ``tests/test_oracle.py``; no function here
+is "parity unpinned".
+"""
+from .attention import attention_f64, brute_force, split_combine_f64, kv_write_ref, visible_keys
+
+__all__ = ["attention_f64", "brute_force", "split_combine_f64", "kv_write_ref", "visible_keys"]
