@@ -1,0 +1,16 @@
+"""Paged KV attention for MI355X (gfx950): hand-written HIP kernels behind a C ABI.
+
+The public functions marshal torch tensors into ``libpagedattn.so``:
+
+* ``paged_attention`` -- causal GQA attention of a flattened ragged batch of
+  query tokens (decode, verify blocks and prefill chunks) over block-paged K/V;
+* ``kv_cache_write`` -- scatter new K/V rows into the pools through a slot map;
+* ``workspace_size`` / ``choose_splits`` / ``validate`` -- planning and checks.
+"""
+from ._lib import (PaDims, PagedAttnError, LIB_PATH, EXPORTED, load_library, paged_attention, kv_cache_write,
+                   workspace_size, choose_splits, validate, make_dims, status_string, device_cu_count,
+                   PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH,
+                   PA_ERR_INVALID_DATA)
+
+__all__ = ["PaDims", "PagedAttnError", "LIB_PATH", "EXPORTED", "load_library", "paged_attention", "kv_cache_write",
+           "workspace_size", "choose_splits", "validate", "make_dims", "status_string", "device_cu_count"]

@@ -1,0 +1,215 @@
+"""ctypes binding of libpagedattn.so (argument marshalling only).
+
+Every step of the attention path runs in the HIP kernels of the library; this
+module only turns torch tensors into pointers, strides and the ``pa_dims``
+block, passes the current HIP stream, and raises on a non-OK status.  There is
+no fallback: if the library is missing, importing the functions fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_INVALID_DATA = range(7)
+PA_F32, PA_BF16 = 0, 1
+
+EXPORTED = ("paged_attention", "kv_cache_write", "pa_workspace_size", "pa_choose_splits", "pa_validate",
+            "pa_status_string", "pa_device_cu_count")
+
+
+class PaDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("max_query_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("table_width", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
+        ("kv_stride_page", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
+    ]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpagedattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_attention_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    vp, i32p = ctypes.c_void_p, ctypes.c_void_p
+    lib.paged_attention.restype = ctypes.c_int
+    lib.paged_attention.argtypes = [vp, vp, vp, i32p, i32p, i32p, ctypes.c_float, ctypes.c_int, vp, vp,
+                                    ctypes.c_size_t, ctypes.POINTER(PaDims), ctypes.c_int, vp]
+    lib.kv_cache_write.restype = ctypes.c_int
+    lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.POINTER(PaDims), ctypes.c_int, vp]
+    lib.pa_workspace_size.restype = ctypes.c_size_t
+    lib.pa_workspace_size.argtypes = [ctypes.POINTER(PaDims), ctypes.c_int]
+    lib.pa_choose_splits.restype = ctypes.c_int32
+    lib.pa_choose_splits.argtypes = [ctypes.POINTER(PaDims)]
+    lib.pa_validate.restype = ctypes.c_int
+    lib.pa_validate.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(PaDims), vp]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_device_cu_count.restype = ctypes.c_int32
+    lib.pa_device_cu_count.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return PA_F32
+    if t == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t}: float32 or bfloat16")
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+              max_query_len: Optional[int] = None, num_splits: int = 0) -> PaDims:
+    if q.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("q must be [N, Hq, D] and the pools [P, ps, Hkv, D]")
+    N, Hq, D = q.shape
+    P, ps, Hkv, Dk = k_pool.shape
+    if Dk != D:
+        raise ValueError(f"head_dim mismatch: q has {D}, pools have {Dk}")
+    if q.stride(2) != 1 or k_pool.stride(3) != 1 or (out is not None and out.stride(2) != 1):
+        raise ValueError("the head dimension must be contiguous")
+    o = out if out is not None else q
+    d = PaDims()
+    d.num_seqs = int(block_tables.shape[0])
+    d.num_tokens = int(N)
+    d.max_query_len = int(max_query_len or 0)
+    d.num_q_heads, d.num_kv_heads, d.head_dim = int(Hq), int(Hkv), int(D)
+    d.page_size, d.num_pages, d.table_width = int(ps), int(P), int(block_tables.shape[1])
+    d.num_splits = int(num_splits)
+    d.q_stride_tok, d.q_stride_head = q.stride(0), q.stride(1)
+    d.o_stride_tok, d.o_stride_head = o.stride(0), o.stride(1)
+    d.kv_stride_page, d.kv_stride_slot, d.kv_stride_head = k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+    return d
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32 (convert int64 metadata once, outside timed regions)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def workspace_size(dims: PaDims, dtype: torch.dtype) -> int:
+    return int(load_library().pa_workspace_size(ctypes.byref(dims), _dtype_code(dtype)))
+
+
+def choose_splits(dims: PaDims) -> int:
+    return int(load_library().pa_choose_splits(ctypes.byref(dims)))
+
+
+def device_cu_count() -> int:
+    return int(load_library().pa_device_cu_count())
+
+
+def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, query_start_loc: torch.Tensor, scale: Optional[float] = None,
+                    causal: bool = True, *, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, max_query_len: Optional[int] = None,
+                    num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Causal GQA attention of q over the paged pools; returns ``out`` [N, Hq, D].
+
+    ``scale`` defaults to 1/sqrt(D).  ``max_query_len`` is a host bound on any
+    sequence's query tokens (default N); ``num_splits`` 0 picks the split count.
+    """
+    lib = load_library()
+    if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
+    if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
+        raise TypeError("q and the pools must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    dims = make_dims(q, k_pool, block_tables, out=out, max_query_len=max_query_len, num_splits=num_splits)
+    bt = _i32(block_tables, "block_tables")
+    cl = _i32(context_lens, "context_lens")
+    qsl = _i32(query_start_loc, "query_start_loc")
+    code = _dtype_code(q.dtype)
+    need = int(lib.pa_workspace_size(ctypes.byref(dims), code))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    st = lib.paged_attention(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), bt.data_ptr(), cl.data_ptr(),
+                             qsl.data_ptr(), float(scale), 1 if causal else 0, out.data_ptr(), ws_ptr, ws_bytes,
+                             ctypes.byref(dims), code, _stream_ptr(stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attention")
+    return out
+
+
+def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   slot_mapping: torch.Tensor, stream=None) -> None:
+    """Scatter k_new/v_new [T, Hkv, D] into the pools at slot_mapping[T] (-1 = skip)."""
+    lib = load_library()
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must have the same shape and strides")
+    if k_new.dtype != k_pool.dtype:
+        raise TypeError("new rows and pools must share one dtype")
+    if k_new.stride(2) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    dims = PaDims()
+    P, ps, Hkv, D = k_pool.shape
+    dims.num_kv_heads, dims.head_dim, dims.page_size, dims.num_pages = int(Hkv), int(D), int(ps), int(P)
+    dims.kv_stride_page, dims.kv_stride_slot, dims.kv_stride_head = k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+    sm = _i32(slot_mapping, "slot_mapping")
+    st = lib.kv_cache_write(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), sm.data_ptr(),
+                            int(k_new.shape[0]), k_new.stride(0), k_new.stride(1), ctypes.byref(dims),
+                            _dtype_code(k_new.dtype), _stream_ptr(stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "kv_cache_write")
+
+
+def validate(block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor, *,
+             num_tokens: int, page_size: int, num_pages: int, slot_mapping: Optional[torch.Tensor] = None,
+             causal: bool = True, stream=None) -> int:
+    """Synchronous metadata check (debug/test only); returns the status code."""
+    lib = load_library()
+    dims = PaDims()
+    dims.num_seqs = int(block_tables.shape[0])
+    dims.table_width = int(block_tables.shape[1])
+    dims.num_tokens = int(num_tokens)
+    dims.page_size, dims.num_pages = int(page_size), int(num_pages)
+    sm_ptr, ns = (None, 0)
+    if slot_mapping is not None:
+        sm = _i32(slot_mapping, "slot_mapping")
+        sm_ptr, ns = sm.data_ptr(), int(sm.numel())
+    return int(lib.pa_validate(_i32(block_tables, "block_tables").data_ptr(), _i32(context_lens, "context_lens").data_ptr(),
+                               _i32(query_start_loc, "query_start_loc").data_ptr(), sm_ptr, ns, 1 if causal else 0,
+                               ctypes.byref(dims), _stream_ptr(stream)))

@@ -1,0 +1,209 @@
+// C-ABI entry points of libpagedattn.so (declared in include/pagedattn.h).
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "host_logic.h"
+#include "pa_device.h"
+
+namespace pa {
+hipError_t launch_decode(const AttnParams& p, int nt, hipStream_t st);
+hipError_t launch_prefill(const AttnParams& p, hipStream_t st);
+hipError_t launch_f32(const AttnParams& p, int max_q, hipStream_t st);
+hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st);
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
+
+static std::atomic<int> g_cu_cache[64];
+
+static int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (dev < 64) g_cu_cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent sizes or strides";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, page_size, group or alignment";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_INVALID_DATA: return "device metadata out of range";
+  }
+  return "unknown status";
+}
+
+int32_t pa_device_cu_count(void) { return cu_count(); }
+
+int32_t pa_choose_splits(const pa_dims* dims) {
+  if (check_dims(dims, PA_BF16) != PA_OK && check_dims(dims, PA_F32) != PA_OK) return 1;
+  const Plan pl = make_plan(dims, PA_BF16, cu_count());
+  return pl.splits;
+}
+
+size_t pa_workspace_size(const pa_dims* dims, pa_dtype dtype) {
+  if (check_dims(dims, dtype) != PA_OK) return 0;
+  return make_plan(dims, dtype, cu_count()).workspace_bytes;
+}
+
+pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
+                          void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims, pa_dtype dtype,
+                          void* stream) {
+  pa_status st = check_dims(dims, dtype);
+  if (st != PA_OK) return st;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0 || dims->num_tokens == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start_loc || !out) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_UNSUPPORTED;
+  const Plan pl = make_plan(dims, dtype, cu_count());
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+
+  AttnParams p{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.out = out;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start_loc = query_start_loc;
+  const int N = dims->num_tokens, Hq = dims->num_q_heads;
+  if (pl.splits > 1) {
+    p.ws_acc = (float*)workspace;
+    p.ws_ml = (float*)workspace + (size_t)pl.splits * N * Hq * dims->head_dim;
+  }
+  p.q_stride_tok = dims->q_stride_tok;
+  p.q_stride_head = dims->q_stride_head;
+  p.o_stride_tok = dims->o_stride_tok;
+  p.o_stride_head = dims->o_stride_head;
+  p.kv_stride_page = dims->kv_stride_page;
+  p.kv_stride_slot = dims->kv_stride_slot;
+  p.kv_stride_head = dims->kv_stride_head;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.num_seqs = dims->num_seqs;
+  p.num_tokens = N;
+  p.num_q_heads = Hq;
+  p.num_kv_heads = dims->num_kv_heads;
+  p.group = Hq / dims->num_kv_heads;
+  p.head_dim = dims->head_dim;
+  p.page_size = dims->page_size;
+  p.num_pages = dims->num_pages;
+  p.table_width = dims->table_width;
+  p.num_splits = pl.splits;
+  p.pages_per_split = pl.pages_per_split;
+  p.causal = causal ? 1 : 0;
+  p.dec_max_n = pl.dec_max_n;
+  p.tok_per_tile = pl.tok_per_tile;
+  p.num_qtiles = pl.num_qtiles;
+  p.comb_max_n = pl.comb_max_n;
+  p.comb_tokens = pl.comb_tokens;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (dtype == PA_F32) {
+    e = launch_f32(p, pl.mql, s);
+    if (e == hipSuccess && pl.combine) e = launch_combine(p, false, s);
+  } else {
+    if (pl.prefill) e = launch_prefill(p, s);
+    if (e == hipSuccess && pl.dec_small) {
+      AttnParams q1 = p;
+      q1.row_lo = 0;
+      q1.row_hi = 16;
+      e = launch_decode(q1, 1, s);
+    }
+    if (e == hipSuccess && pl.dec_big) {
+      AttnParams q2 = p;
+      q2.row_lo = 16;
+      q2.row_hi = 16 * pl.big_nt;
+      e = launch_decode(q2, pl.big_nt, s);
+    }
+    if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
+  }
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                         const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
+                         int64_t new_stride_head, const pa_dims* dims, pa_dtype dtype, void* stream) {
+  if (!dims) return PA_ERR_NULL;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || new_stride_tok < 0 || new_stride_head < 0) return PA_ERR_SHAPE;
+  if (dims->num_kv_heads < 1 || dims->num_pages < 0) return PA_ERR_SHAPE;
+  if (dims->head_dim != 64 && dims->head_dim != 128 && dims->head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (dims->page_size != 16 && dims->page_size != 32 && dims->page_size != 64 && dims->page_size != 128)
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return PA_ERR_NULL;
+  const int64_t vec = dtype == PA_BF16 ? 8 : 4;
+  const int64_t s[] = {new_stride_tok, new_stride_head, dims->kv_stride_page, dims->kv_stride_slot,
+                       dims->kv_stride_head};
+  for (int64_t x : s)
+    if (x % vec) return PA_ERR_UNSUPPORTED;
+  if ((dims->num_kv_heads > 1 && (new_stride_head < dims->head_dim || dims->kv_stride_head < dims->head_dim)))
+    return PA_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_UNSUPPORTED;
+  KvWriteParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.slot_mapping = slot_mapping;
+  p.new_stride_tok = new_stride_tok;
+  p.new_stride_head = new_stride_head;
+  p.kv_stride_page = dims->kv_stride_page;
+  p.kv_stride_slot = dims->kv_stride_slot;
+  p.kv_stride_head = dims->kv_stride_head;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = dims->num_kv_heads;
+  p.head_dim = dims->head_dim;
+  p.page_size = dims->page_size;
+  p.num_pages = dims->num_pages;
+  p.elem_bytes = dtype == PA_BF16 ? 2 : 4;
+  return launch_kv_write(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                      const int32_t* slot_mapping, int32_t num_slots, int causal, const pa_dims* dims,
+                      void* stream) {
+  if (!dims) return PA_ERR_NULL;
+  if (dims->num_seqs < 0 || dims->table_width < 0 || dims->num_pages < 0 || num_slots < 0) return PA_ERR_SHAPE;
+  if (dims->page_size < 1) return PA_ERR_UNSUPPORTED;
+  const int B = dims->num_seqs, W = dims->table_width;
+  if (B > 0 && (!block_tables || !context_lens || !query_start_loc)) return PA_ERR_NULL;
+  if (num_slots > 0 && !slot_mapping) return PA_ERR_NULL;
+  std::vector<int32_t> bt((size_t)B * W), lens(B), qsl(B + 1), sl(num_slots > 0 ? num_slots : 0);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (B > 0) {
+    if (W > 0) e = hipMemcpyAsync(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(lens.data(), context_lens, lens.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(qsl.data(), query_start_loc, qsl.size() * 4, hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess && num_slots > 0) e = hipMemcpyAsync(sl.data(), slot_mapping, sl.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  return validate_host(bt.data(), lens.data(), qsl.data(), num_slots > 0 ? sl.data() : nullptr, num_slots, causal,
+                       dims);
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// Float32 paged attention on the vector ALUs (gfx950).
+//
+// Float32 has no MFMA path worth its precision cost here, so each query row
+// (token, query head, split) is one wave.  The wave walks its split's keys in
+// chunks of 64: lane j scores key j of the chunk against the row's query
+// (held in LDS, read as a broadcast), the chunk's maximum and the softmax
+// state are wave reductions, and lane d accumulates output dims d, d+64, ...
+// with the chunk's probabilities read lane by lane.  Everything stays float32
+// (page "paged-attn-xpu", Requirements and limits: scores and softmax state
+// float32, split partials float32) and only keys below the row's visible end
+// are ever read, so slots past the context are never touched.
+#include "pa_device.h"
+
+namespace pa {
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
+  constexpr int DPL = D / 64;                    // output dims per lane
+  __shared__ float qs[D];
+  // grid: x = split + S * (head + Hq * token_slot), y = sequence
+  const int S = p.num_splits;
+  int x = blockIdx.x;
+  const int split = x % S;
+  x /= S;
+  const int h = x % p.num_q_heads;
+  const int t = x / p.num_q_heads;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+
+  const int s0 = p.query_start_loc[b];
+  const int n = p.query_start_loc[b + 1] - s0;
+  if (t >= n) return;
+  const int ps = p.page_size;
+  const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
+  const int kend = p.causal ? clampi(L - n + t + 1, 0, L) : L;
+  const int kpp = p.pages_per_split * ps;
+  const int k_begin = split * kpp;
+  const int k_stop = min(k_begin + kpp, kend);
+  const int g = h / p.group;
+  const int tok = s0 + t;
+
+  const float* qp = (const float*)p.q + (int64_t)tok * p.q_stride_tok + (int64_t)h * p.q_stride_head;
+  for (int d = lane; d < D; d += 64) qs[d] = qp[d];
+  __syncthreads();
+
+  const float* kb = (const float*)p.k_pool + (int64_t)g * p.kv_stride_head;
+  const float* vb = (const float*)p.v_pool + (int64_t)g * p.kv_stride_head;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  for (int j0 = k_begin; j0 < k_stop; j0 += 64) {
+    const int j = j0 + lane;
+    float s = kNegInf;
+    int64_t off = 0;
+    if (j < k_stop) {
+      const int lp = j / ps;
+      off = (int64_t)page_of(p, b, lp) * p.kv_stride_page + (int64_t)(j - lp * ps) * p.kv_stride_slot;
+      const f32x4* kr = (const f32x4*)(kb + off);
+      float dot = 0.f;
+#pragma unroll 4
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const f32x4 kv = kr[d4];
+        dot = fmaf(qs[4 * d4], kv[0], dot);
+        dot = fmaf(qs[4 * d4 + 1], kv[1], dot);
+        dot = fmaf(qs[4 * d4 + 2], kv[2], dot);
+        dot = fmaf(qs[4 * d4 + 3], kv[3], dot);
+      }
+      s = dot * p.scale_log2;
+    }
+    const float cmax = wave_max(s);
+    const float m_new = fmaxf(m_run, cmax);
+    const float m_safe = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_safe);
+    const float pj = fast_exp2(s - m_safe);
+    l_run = alpha * l_run + wave_sum(pj);
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] *= alpha;
+    const int cnt = min(64, k_stop - j0);
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj));
+      const int64_t o = (int64_t)__builtin_amdgcn_readlane((int)(off & 0xffffffff), jj) |
+                        ((int64_t)__builtin_amdgcn_readlane((int)(off >> 32), jj) << 32);
+      const float* vr = vb + o;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pw, vr[lane + 64 * i], acc[i]);
+    }
+  }
+
+  const int64_t NH = (int64_t)p.num_tokens * p.num_q_heads;
+  if (S == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* op = (float*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) op[lane + 64 * i] = acc[i] * inv;
+  } else {
+    const int64_t ri = (int64_t)split * NH + (int64_t)tok * p.num_q_heads + h;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) p.ws_acc[ri * D + lane + 64 * i] = acc[i];
+    if (lane == 0) {
+      p.ws_ml[ri * 2] = m_run;
+      p.ws_ml[ri * 2 + 1] = l_run;
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_f32_t(const AttnParams& p, int max_q, hipStream_t st) {
+  const int64_t gx = (int64_t)p.num_splits * p.num_q_heads * max_q;
+  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3((unsigned)gx, p.num_seqs), dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32(const AttnParams& p, int max_q, hipStream_t st) {
+  switch (p.head_dim) {
+    case 64: return launch_f32_t<64>(p, max_q, st);
+    case 128: return launch_f32_t<128>(p, max_q, st);
+    case 256: return launch_f32_t<256>(p, max_q, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split combine.  For output row (token, head) with partials (acc_s, m_s, l_s):
+//   M = max_s m_s (0 if every split is empty), w_s = exp2(m_s - M),
+//   out = sum_s w_s acc_s / sum_s w_s l_s, and zero when the sum is zero.
+// This is the log-sum-exp merge of page "32. Production attention kernels"
+// (Long contexts: split the keys) written for unnormalised partials, as in
+// page "Attention and KV Cache" (Split-KV decode, Combine).  Splits are summed
+// in index order, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(64) void combine_kernel(const AttnParams p) {
+  constexpr int DPL = D / 64;
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int s0 = p.query_start_loc[b];
+  const int n = p.query_start_loc[b + 1] - s0;
+  if (t >= n || n > p.comb_max_n) return;
+  const int tok = s0 + t;
+  const int64_t NH = (int64_t)p.num_tokens * p.num_q_heads;
+  const int64_t row = (int64_t)tok * p.num_q_heads + h;
+  const int S = p.num_splits;
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(s * NH + row) * 2]);
+  const float Ms = M == kNegInf ? 0.f : M;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  float l = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const int64_t ri = s * NH + row;
+    const float w = fast_exp2(p.ws_ml[ri * 2] - Ms);
+    l = fmaf(w, p.ws_ml[ri * 2 + 1], l);
+    const float* a = p.ws_acc + ri * D;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, a[lane * DPL + i], acc[i]);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (BF16) {
+    __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) op[i] = (__bf16)(acc[i] * inv);
+  } else {
+    float* op = (float*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) op[i] = acc[i] * inv;
+  }
+}
+
+template <int D>
+static hipError_t launch_combine_t(const AttnParams& p, bool bf16, hipStream_t st) {
+  dim3 grid(p.num_q_heads, p.comb_tokens, p.num_seqs);
+  if (bf16)
+    hipLaunchKernelGGL((combine_kernel<D, true>), grid, dim3(64), 0, st, p);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, false>), grid, dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st) {
+  switch (p.head_dim) {
+    case 64: return launch_combine_t<64>(p, bf16, st);
+    case 128: return launch_combine_t<128>(p, bf16, st);
+    case 256: return launch_combine_t<256>(p, bf16, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KV write: token i's K and V rows ([Hkv, D]) go to flat slot s =
+// slot_mapping[i] = page * ps + offset of both pools; s < 0 writes nothing
+// (page "Attention and KV Cache", Paged KV: the write map, -1 for padding
+// tokens; cost follows the tokens, not the pool).  One workgroup per token,
+// 16-byte copies; slots outside the pool are skipped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteParams p) {
+  const int i = blockIdx.x;
+  const int slot = p.slot_mapping[i];
+  if (slot < 0 || slot >= p.num_pages * p.page_size) return;
+  const int page = slot / p.page_size, off = slot % p.page_size;
+  const int cpr = p.head_dim * p.elem_bytes / 16;     // 16-byte chunks per head row
+  const int total = p.num_kv_heads * cpr;
+  const int64_t eb = p.elem_bytes;
+  const char* ksrc = (const char*)p.k_new + i * p.new_stride_tok * eb;
+  const char* vsrc = (const char*)p.v_new + i * p.new_stride_tok * eb;
+  char* kdst = (char*)p.k_pool + ((int64_t)page * p.kv_stride_page + (int64_t)off * p.kv_stride_slot) * eb;
+  char* vdst = (char*)p.v_pool + ((int64_t)page * p.kv_stride_page + (int64_t)off * p.kv_stride_slot) * eb;
+  for (int c = threadIdx.x; c < total; c += 256) {
+    const int hh = c / cpr, cc = c % cpr;
+    const int64_t so = hh * p.new_stride_head * eb + cc * 16;
+    const int64_t dst = hh * p.kv_stride_head * eb + cc * 16;
+    *(u32x4*)(kdst + dst) = *(const u32x4*)(ksrc + so);
+    *(u32x4*)(vdst + dst) = *(const u32x4*)(vsrc + so);
+  }
+}
+
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(kv_write_kernel, dim3(p.num_tokens), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

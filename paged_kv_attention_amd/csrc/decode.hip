@@ -1,0 +1,331 @@
+// GQA-packed split-KV decode / verify attention for gfx950 (bf16 K/V, MFMA).
+//
+// One workgroup per (split, KV head g, sequence b); 4 waves.  The rows of the
+// query tile are all n tokens of the step times the G query heads that share
+// KV head g, row r = token (r / G), head g*G + r % G, padded to 16*NT rows, so
+// every K/V page of the split is read from memory once for the whole group
+// (page "Attention kernels", Decode: GQA packing and split-KV; page "32.
+// Production attention kernels", One kernel for the whole batch).
+//
+// The split's keys are cut into 32-key chunks; wave w walks chunks w, w+4,
+// ... with its own online-softmax state (running max m, sum l, accumulator),
+// prefetching its next chunk's K and V into registers while it computes the
+// current one.  Per chunk:
+//   S^T[32 keys x rows] = K . Q^T   on v_mfma_f32_16x16x32_bf16, K loaded
+//                                   from the page straight into the A operand
+//                                   (8 contiguous dims per lane);
+//   mask (only chunks that reach the causal diagonal or the split's end);
+//   m' = max(m, rowmax), alpha = exp2(m - m'), p = exp2(s - m') in float32;
+//   O^T[D x rows] += V^T . P^T      V staged through the wave's LDS tile and
+//                                   read back transposed (ds_read_b64_tr_b16);
+//                                   P^T is already in the B-operand layout of
+//                                   S^T's accumulator registers.
+// Scores use exp2 with scale*log2(e) folded in (page "Attention kernels", One
+// kernel family: scores in Float32 with exp2), and p is rounded to bf16 only
+// for the PV product (same passage); l sums the rounded p, so the weights
+// the product uses are exactly the ones the output is normalised by.  The
+// -inf guard follows page "32. Production attention kernels" (m_safe), and V
+// rows past the split's end are selected to zero before the product, so a
+// NaN in an unused slot cannot reach an output (page "Attention and KV
+// Cache", live length: a true select, not a multiply by zero).
+//
+// The four waves' states are merged in LDS in a fixed order.  With one split
+// the normalised output is written directly; otherwise the unnormalised
+// partial (acc, m, l) goes to the float32 workspace for the combine kernel,
+// and a split without keys writes the neutral (0, -inf, 0) (page "Attention
+// and KV Cache", Split-KV decode).
+#include "pa_device.h"
+
+namespace pa {
+
+template <int D>
+struct DecodeCfg {
+  static constexpr int KC = 32;                  // keys per chunk: two 16-key MFMA tiles
+  static constexpr int DS = D / 32;              // 32-dim k-steps of QK^T
+  static constexpr int DT = D / 16;              // 16-dim output tiles of PV
+  static constexpr int CPL = D / 8;              // 16-byte chunks per key row
+  static constexpr int VLOADS = KC * CPL / 64;   // 16-byte V loads per lane per chunk
+  static constexpr int ROW_BYTES = D * 2 + 32;   // V staging row stride (32 B pad: no bank conflicts
+                                                 // between the 4 rows a transpose read touches)
+  static constexpr int WAVE_LDS = KC * ROW_BYTES;
+};
+
+template <int D, int NT>
+struct DecodeLds {
+  static constexpr int ROWS = 16 * NT;
+  static constexpr int ORS = D + 4;              // merge buffer row stride in floats
+  static constexpr int STAGE = 4 * DecodeCfg<D>::WAVE_LDS;
+  static constexpr int MERGE = (8 * ROWS + ROWS * ORS) * 4;
+  static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
+};
+
+template <int D>
+struct DecodeChunk {
+  bf16x8 k[2][DecodeCfg<D>::DS];
+  u32x4 v[DecodeCfg<D>::VLOADS];
+};
+
+template <int D, int NT>
+__global__ __launch_bounds__(256) void decode_splitkv_kernel(const AttnParams p) {
+  using C = DecodeCfg<D>;
+  constexpr int ROWS = 16 * NT;
+  constexpr int ORS = DecodeLds<D, NT>::ORS;
+  __shared__ __attribute__((aligned(16))) char smem[DecodeLds<D, NT>::BYTES];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, q4 = lane >> 4;
+
+  const int s0 = p.query_start_loc[b];
+  const int n = p.query_start_loc[b + 1] - s0;
+  const int G = p.group;
+  const int rows = n * G;
+  if (n <= 0 || n > p.dec_max_n || rows <= p.row_lo || rows > p.row_hi) return;
+
+  const int ps = p.page_size;
+  const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
+  const int npages = (L + ps - 1) / ps;
+  const int pg0 = split * p.pages_per_split;
+  const int pg1 = min(pg0 + p.pages_per_split, npages);
+  const int k_begin = pg0 * ps;
+  const int k_end = min(pg1 * ps, L);
+  const int nchunks = k_end > k_begin ? (k_end - k_begin + C::KC - 1) / C::KC : 0;
+  const int causal = p.causal;
+  const int diag = L - n;                       // token t sees keys j <= diag + t
+  // keys below mask_lim are visible to every row of this tile
+  const int mask_lim = min(k_end, causal ? diag + 1 : L);
+
+  // ---- query tile as the B operand of S^T = K . Q^T (row = lane % 16)
+  bf16x8 qB[NT][C::DS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = 16 * nt + l16;
+    if (r < rows) {
+      const int tok = s0 + r / G, head = g * G + r % G;
+      const __bf16* qp = (const __bf16*)p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) qB[nt][s] = *(const bf16x8*)(qp + 32 * s + 8 * q4);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) qB[nt][s] = bf16x8{};
+    }
+  }
+
+  f32x4 acc[NT][C::DT];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = kNegInf;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  PA_LDS char* vl = (PA_LDS char*)smem + wave * C::WAVE_LDS;
+  const __bf16* kbase = (const __bf16*)p.k_pool + (int64_t)g * p.kv_stride_head;
+  const __bf16* vbase = (const __bf16*)p.v_pool + (int64_t)g * p.kv_stride_head;
+
+  // Address of slot `sl` of the page holding 16-key tile starting at key `kt`
+  // (tiles never straddle pages: ps is a multiple of 16).  A tile past the
+  // sequence's last page re-reads that page; its keys are masked.
+  auto tile_off = [&](int kt, int sl) -> int64_t {
+    int lp = kt / ps;
+    const int slot = kt - lp * ps + sl;
+    lp = min(lp, npages - 1);
+    const int pg = page_of(p, b, lp);
+    return (int64_t)pg * p.kv_stride_page + (int64_t)slot * p.kv_stride_slot;
+  };
+
+  auto load = [&](int c, DecodeChunk<D>& ch) {
+    const int k0 = k_begin + c * C::KC;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const __bf16* kp = kbase + tile_off(k0 + 16 * t, l16) + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const bf16x8*)(kp + 32 * s);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VLOADS; ++i) {
+      const int idx = i * 64 + lane;
+      const int kl = idx / C::CPL, cc = idx % C::CPL;
+      const int t = (i * 64 / C::CPL) / 16;       // uniform per load
+      const __bf16* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) + 8 * cc;
+      ch.v[i] = *(const u32x4*)vp;
+    }
+  };
+
+  auto process = [&](int c, const DecodeChunk<D>& ch) {
+    const int k0 = k_begin + c * C::KC;
+    const bool need_mask = k0 + C::KC > mask_lim;
+    // V chunk -> this wave's LDS tile, rows past the split's end selected to zero
+#pragma unroll
+    for (int i = 0; i < C::VLOADS; ++i) {
+      const int idx = i * 64 + lane;
+      const int kl = idx / C::CPL, cc = idx % C::CPL;
+      u32x4 v = ch.v[i];
+      if (need_mask && k0 + kl >= k_end) v = u32x4{0u, 0u, 0u, 0u};
+      *(PA_LDS u32x4*)(vl + kl * C::ROW_BYTES + cc * 16) = v;
+    }
+    // S^T = K . Q^T
+    f32x4 st[2][NT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) a = mfma16(ch.k[t][s], qB[nt][s], a);
+        st[t][nt] = a;
+      }
+    bf16x8 pB[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x[2][4];
+      const int tok = (16 * nt + l16) / G;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = st[t][nt][r] * p.scale_log2;
+          if (need_mask) {
+            const int j = k0 + 16 * t + 4 * q4 + r;
+            const bool vis = j < k_end && (!causal || j <= diag + tok);
+            v = vis ? v : kNegInf;
+          }
+          x[t][r] = v;
+        }
+      float cmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run[nt], cmax);
+      const float m_safe = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[nt] - m_safe);
+      m_run[nt] = m_new;
+      uint32_t pk[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        pk[2 * t] = pack_bf16x2(fast_exp2(x[t][0] - m_safe), fast_exp2(x[t][1] - m_safe));
+        pk[2 * t + 1] = pack_bf16x2(fast_exp2(x[t][2] - m_safe), fast_exp2(x[t][3] - m_safe));
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) psum += bf16_lo(pk[i]) + bf16_hi(pk[i]);
+      l_run[nt] = alpha * l_run[nt] + psum;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] *= alpha;
+      pB[nt] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    }
+    // O^T += V^T . P^T ; V^T read transposed from LDS:
+    // lane (q4, l16) gets V[4*q4 + e][16*dt + l16] and V[16 + 4*q4 + e][...]
+    const PA_LDS char* r1 = vl + (4 * q4 + (l16 >> 2)) * C::ROW_BYTES + 8 * (l16 & 3);
+    const PA_LDS char* r2 = r1 + 16 * C::ROW_BYTES;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const u32x2 a1 = lds_read_tr16(r1 + 32 * dt);
+      const u32x2 a2 = lds_read_tr16(r2 + 32 * dt);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a1.x, a1.y, a2.x, a2.y});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma16(va, pB[nt], acc[nt][dt]);
+    }
+  };
+
+  int c = wave;
+  if (c < nchunks) {
+    DecodeChunk<D> ca, cb;
+    load(c, ca);
+    while (true) {
+      const bool hb = c + 4 < nchunks;
+      if (hb) load(c + 4, cb);
+      process(c, ca);
+      c += 4;
+      if (!hb) break;
+      const bool ha = c + 4 < nchunks;
+      if (ha) load(c + 4, ca);
+      process(c, cb);
+      c += 4;
+      if (!ha) break;
+    }
+  }
+
+  // ---- merge the four waves' states (fixed order: bitwise repeatable)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    l_run[nt] += shfl_xor(l_run[nt], 16);
+    l_run[nt] += shfl_xor(l_run[nt], 32);
+  }
+  __syncthreads();                              // staging tiles are free from here on
+  float* Mw = (float*)smem;                     // [4][ROWS]
+  float* Lw = Mw + 4 * ROWS;                    // [4][ROWS]
+  float* Ob = Lw + 4 * ROWS;                    // [ROWS][ORS]
+  if (q4 == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) Mw[wave * ROWS + 16 * nt + l16] = m_run[nt];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = 16 * nt + l16;
+    float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
+    const float Ms = M == kNegInf ? 0.f : M;
+    const float e = fast_exp2(m_run[nt] - Ms);
+    l_run[nt] *= e;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] *= e;
+    if (q4 == 0) Lw[wave * ROWS + row] = l_run[nt];
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          f32x4* o = (f32x4*)(Ob + (16 * nt + l16) * ORS + 16 * dt + 4 * q4);
+          *o = (w == 0) ? acc[nt][dt] : (*o + acc[nt][dt]);
+        }
+    }
+    __syncthreads();
+  }
+
+  const int nrows = min(rows, ROWS);
+  const int NH = p.num_tokens * p.num_q_heads;
+  for (int it = threadIdx.x; it < nrows * (D / 4); it += 256) {
+    const int row = it / (D / 4), c4 = it % (D / 4);
+    const int tok = s0 + row / G, head = g * G + row % G;
+    const float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
+    const float Lt = ((Lw[row] + Lw[ROWS + row]) + Lw[2 * ROWS + row]) + Lw[3 * ROWS + row];
+    const f32x4 o = *(const f32x4*)(Ob + row * ORS + 4 * c4);
+    if (p.num_splits == 1) {
+      const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+      __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
+      *(u32x2*)op = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+    } else {
+      const int64_t ri = (int64_t)split * NH + (int64_t)tok * p.num_q_heads + head;
+      *(f32x4*)(p.ws_acc + ri * D + 4 * c4) = o;
+      if (c4 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{M, Lt};
+    }
+  }
+}
+
+template <int D, int NT>
+static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
+  dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
+  hipLaunchKernelGGL((decode_splitkv_kernel<D, NT>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnParams& p, int nt, hipStream_t st) {
+  switch (p.head_dim) {
+    case 64:
+      return nt == 1 ? launch_decode_t<64, 1>(p, st) : nt == 2 ? launch_decode_t<64, 2>(p, st) : launch_decode_t<64, 4>(p, st);
+    case 128:
+      return nt == 1 ? launch_decode_t<128, 1>(p, st) : nt == 2 ? launch_decode_t<128, 2>(p, st) : launch_decode_t<128, 4>(p, st);
+    case 256:
+      return nt == 1 ? launch_decode_t<256, 1>(p, st) : nt == 2 ? launch_decode_t<256, 2>(p, st) : launch_decode_t<256, 4>(p, st);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,132 @@
+// Host-only planning for paged_attention (see host_logic.h).
+#include "host_logic.h"
+
+#include <limits.h>
+
+#include <vector>
+
+namespace pa {
+
+static bool one_of(int v, std::initializer_list<int> set) {
+  for (int x : set)
+    if (v == x) return true;
+  return false;
+}
+
+pa_status check_dims(const pa_dims* d, pa_dtype dtype) {
+  if (!d) return PA_ERR_NULL;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs < 0 || d->num_tokens < 0 || d->max_query_len < 0 || d->num_splits < 0) return PA_ERR_SHAPE;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (d->num_pages < 0 || d->table_width < 0) return PA_ERR_SHAPE;
+  if (d->num_seqs > 0 && (d->num_pages < 1 || d->table_width < 1)) return PA_ERR_SHAPE;
+  if (!one_of(d->head_dim, {64, 128, 256})) return PA_ERR_UNSUPPORTED;
+  if (!one_of(d->page_size, {16, 32, 64, 128})) return PA_ERR_UNSUPPORTED;
+  const int64_t D = d->head_dim;
+  const int64_t s[] = {d->q_stride_tok, d->q_stride_head, d->o_stride_tok, d->o_stride_head,
+                       d->kv_stride_page, d->kv_stride_slot, d->kv_stride_head};
+  for (int64_t x : s)
+    if (x < 0) return PA_ERR_SHAPE;
+  // rows of one head must not overlap: D is contiguous
+  if ((d->num_q_heads > 1 && (d->q_stride_head < D || d->o_stride_head < D)) ||
+      (d->num_tokens > 1 && (d->q_stride_tok < D || d->o_stride_tok < D)) ||
+      (d->num_kv_heads > 1 && d->kv_stride_head < D) || d->kv_stride_slot < D ||
+      (d->num_pages > 1 && d->kv_stride_page < D))
+    return PA_ERR_SHAPE;
+  // 16-byte vector loads: every stride a whole number of 16-byte chunks
+  const int64_t vec = dtype == PA_BF16 ? 8 : 4;
+  for (int64_t x : s)
+    if (x % vec) return PA_ERR_UNSUPPORTED;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (dtype == PA_BF16 && G > 64) return PA_ERR_UNSUPPORTED;
+  // grid limits (y and z dimensions are 16-bit)
+  if (d->num_seqs > 65535 || d->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)d->table_width * d->page_size > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count) {
+  const int W = d->table_width > 0 ? d->table_width : 1;
+  if (d->num_splits > 0) return d->num_splits < W ? d->num_splits : W;
+  if (cu_count < 1) cu_count = 1;
+  // units of parallel work per split: (sequence, KV head) workgroups of 4 waves
+  // for the bf16 decode kernel, (token, query head) waves for float32.
+  int64_t units = dtype == PA_BF16 ? (int64_t)d->num_seqs * d->num_kv_heads
+                                   : (int64_t)d->num_seqs * d->num_q_heads;
+  int64_t target = dtype == PA_BF16 ? 2 * (int64_t)cu_count : 8 * (int64_t)cu_count;
+  if (units < 1) units = 1;
+  int64_t want = (target + units - 1) / units;
+  const int min_pages = (256 + d->page_size - 1) / d->page_size;
+  const int64_t cap_pages = (W + min_pages - 1) / min_pages;
+  int64_t s = want;
+  if (s > 32) s = 32;
+  if (s > cap_pages) s = cap_pages;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count) {
+  Plan pl{};
+  const int N = d->num_tokens;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int W = d->table_width > 0 ? d->table_width : 1;
+  pl.mql = d->max_query_len > 0 && d->max_query_len < N ? d->max_query_len : N;
+  int S = choose_splits(d, dtype, cu_count);
+  pl.pages_per_split = (W + S - 1) / S;
+  pl.splits = (W + pl.pages_per_split - 1) / pl.pages_per_split;
+  if (dtype == PA_BF16) {
+    int dm = 64 / G;
+    pl.dec_max_n = dm < 16 ? dm : 16;
+    const int dmax = pl.mql < pl.dec_max_n ? pl.mql : pl.dec_max_n;
+    pl.dec_small = dmax >= 1 && G <= 16;
+    pl.dec_big = dmax * G > 16;
+    pl.big_nt = dmax * G <= 32 ? 2 : 4;
+    pl.prefill = pl.mql > pl.dec_max_n;
+    pl.tok_per_tile = 128 / G;
+    pl.num_qtiles = pl.prefill ? (pl.mql + pl.tok_per_tile - 1) / pl.tok_per_tile : 0;
+    pl.combine = pl.splits > 1 && dmax >= 1;
+    pl.comb_tokens = dmax;
+    pl.comb_max_n = pl.dec_max_n;
+  } else {
+    pl.dec_max_n = 0;
+    pl.combine = pl.splits > 1 && pl.mql >= 1;
+    pl.comb_tokens = pl.mql;
+    pl.comb_max_n = INT_MAX;
+  }
+  if (pl.splits > 1)
+    pl.workspace_bytes = (size_t)pl.splits * (size_t)N * (size_t)d->num_q_heads * ((size_t)d->head_dim + 2) * 4;
+  return pl;
+}
+
+pa_status validate_host(const int32_t* bt, const int32_t* lens, const int32_t* qsl, const int32_t* slots,
+                        int32_t num_slots, int causal, const pa_dims* d) {
+  const int B = d->num_seqs, W = d->table_width, ps = d->page_size, P = d->num_pages;
+  if (B > 0 && qsl[0] != 0) return PA_ERR_INVALID_DATA;
+  for (int b = 0; b < B; ++b) {
+    const int n = qsl[b + 1] - qsl[b];
+    if (n < 0) return PA_ERR_INVALID_DATA;
+    const int L = lens[b];
+    if (L < 0 || (int64_t)L > (int64_t)W * ps) return PA_ERR_INVALID_DATA;
+    if (causal && n > L) return PA_ERR_INVALID_DATA;
+    const int npg = (L + ps - 1) / ps;
+    for (int j = 0; j < npg; ++j) {
+      const int pg = bt[(int64_t)b * W + j];
+      if (pg < 0 || pg >= P) return PA_ERR_INVALID_DATA;
+    }
+  }
+  if (B > 0 && qsl[B] != d->num_tokens) return PA_ERR_INVALID_DATA;
+  if (slots && num_slots > 0) {
+    const int64_t cap = (int64_t)P * ps;
+    std::vector<unsigned char> seen((size_t)cap, 0);
+    for (int i = 0; i < num_slots; ++i) {
+      const int s = slots[i];
+      if (s == -1) continue;
+      if (s < 0 || s >= cap) return PA_ERR_INVALID_DATA;
+      if (seen[(size_t)s]) return PA_ERR_INVALID_DATA;
+      seen[(size_t)s] = 1;
+    }
+  }
+  return PA_OK;
+}
+
+}  // namespace pa

@@ -1,0 +1,45 @@
+// Host-only planning for paged_attention: argument checks, the split count
+// and which kernels a call launches.  Plain C++ (no HIP), so it also builds
+// with g++ for host unit tests.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pagedattn.h"
+
+namespace pa {
+
+struct Plan {
+  int mql;                 // effective max_query_len
+  int splits;              // S after sizing (>= 1)
+  int pages_per_split;     // ceil(W / S)
+  int dec_max_n;           // bf16: sequences with n <= dec_max_n use the decode kernel
+  bool dec_small;          // bf16: decode launch for n*G <= 16 (16-row tile)
+  bool dec_big;            // bf16: decode launch for 16 < n*G <= 16*big_nt
+  int big_nt;              // 2 or 4 row tiles
+  bool prefill;            // bf16: prefill launch for n > dec_max_n
+  int tok_per_tile;        // prefill: tokens per 128-row tile
+  int num_qtiles;          // prefill: tiles per sequence (from mql)
+  bool combine;            // split partials need the combine launch
+  int comb_tokens;         // combine: token slots per sequence
+  int comb_max_n;          // combine: sequences with n <= comb_max_n
+  size_t workspace_bytes;  // bytes the call needs
+};
+
+// Checks dims and dtype; PA_OK or the error status (nothing else is touched).
+pa_status check_dims(const pa_dims* d, pa_dtype dtype);
+
+// Split count from host scalars only: enough workgroups to fill `cu_count`
+// CUs about twice, at least 256 keys per split, at most 32 splits; an
+// explicit dims->num_splits > 0 wins (capped at W).
+int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count);
+
+// Full launch plan for valid dims (call check_dims first).
+Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count);
+
+// Host-side check of copied metadata (the body of pa_validate).
+pa_status validate_host(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                        const int32_t* slot_mapping, int32_t num_slots, int causal, const pa_dims* d);
+
+}  // namespace pa

@@ -1,0 +1,85 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16
+// conversion, MFMA wrappers, LDS transpose reads and the packed kernel
+// argument block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_params.h"
+
+namespace pa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+#define PA_LDS __attribute__((address_space(3)))
+
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two float32 -> packed bf16x2 (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 h = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+  __bf16 h = (__bf16)a;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4 x b16 LDS read (gfx950 ds_read_b64_tr_b16).  Within every
+// 16-lane group, lane i receives, as element e, the 16-bit word (i % 4) at the
+// address supplied by lane 4*e + i/4 of the same group.  A group whose lanes
+// point at rows r..r+3 (4 lanes per row, 4 consecutive columns each) thus
+// returns column i of those 4 rows to lane i.
+__device__ __forceinline__ u32x2 lds_read_tr16(const PA_LDS char* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane helpers over the 64-lane wave.
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  int lane = __lane_id();
+  int src = lane ^ mask;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Page id of logical page j of sequence b, clamped into the pool so a bad
+// table entry can never address memory outside it.
+__device__ __forceinline__ int page_of(const AttnParams& p, int b, int j) {
+  int pg = p.block_tables[(int64_t)b * p.table_width + j];
+  return clampi(pg, 0, p.num_pages - 1);
+}
+
+}  // namespace pa

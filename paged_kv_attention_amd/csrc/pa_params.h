@@ -1,0 +1,50 @@
+// Kernel argument blocks.  Each kernel takes one of these by value, so a
+// launch carries a single packed argument however many sizes and strides it
+// needs (page "cuTile design choices", Keep launches under 32 kernel
+// parameters: wide argument lists made every launch slow there).
+#pragma once
+
+#include <stdint.h>
+
+namespace pa {
+
+struct AttnParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  void* out;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  float* ws_acc;            // [S][N*Hq][D] float32 split accumulators
+  float* ws_ml;             // [S][N*Hq][2] float32 (running max in log2 units, sum)
+  int64_t q_stride_tok, q_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t kv_stride_page, kv_stride_slot, kv_stride_head;
+  float scale_log2;         // scale * log2(e): scores go straight into exp2
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, group;
+  int32_t head_dim, page_size, num_pages, table_width;
+  int32_t num_splits;       // S (>= 1)
+  int32_t pages_per_split;  // ceil(W / S)
+  int32_t causal;
+  int32_t dec_max_n;        // sequences with n <= dec_max_n are the decode class
+  int32_t row_lo, row_hi;   // decode kernel: takes sequences with row_lo < n*G <= row_hi
+  int32_t tok_per_tile;     // prefill: query tokens per tile
+  int32_t num_qtiles;       // prefill: tiles per (sequence, KV head)
+  int32_t comb_max_n;       // combine: sequences with n <= comb_max_n
+  int32_t comb_tokens;      // combine: token slots per sequence in the grid
+};
+
+struct KvWriteParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* slot_mapping;
+  int64_t new_stride_tok, new_stride_head;
+  int64_t kv_stride_page, kv_stride_slot, kv_stride_head;
+  int32_t num_tokens, num_kv_heads, head_dim, page_size, num_pages;
+  int32_t elem_bytes;
+};
+
+}  // namespace pa
