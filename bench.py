@@ -1,0 +1,333 @@
+"""Benchmark of the paged KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5]
+
+A step is one pass of the whole path over one batch: kv_cache_write of the
+step's new K/V rows, then paged_attention (decode kernel, plus the combine when
+split) for the headline decode workload -- 64 sequences x 4096 context,
+32 query / 8 KV heads, head dim 128, page 64, bf16 (the Qwen3-8B-shaped step of
+page "32. Production attention kernels").  Pools are rotated over 4 distinct
+sets ("layers", 4.3 GB) so the 256 MB Infinity Cache cannot hold the working
+set.  A second measured object covers long causal prefill (4 x 8192 tokens,
+same heads), reported in TFLOP/s.
+
+Prints ONE JSON line.  `value` is decode GB/s of algorithmic bytes (K and V
+once per GQA group + q + out + page ids + lengths) over the timed step time.
+`roofline` is for the decode kernel: algorithmic bytes per launch over its
+average launch time, measured with HIP events on the launch stream.
+`cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention HBM GB/s (% of peak) at 64×4096 ctx; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+DECODE_KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_traffic.json")
+
+
+# ----------------------------------------------------------------------------- accounting
+def algorithmic_bytes(context_lens, query_lens, num_q_heads, num_kv_heads, head_dim, page_size, elem_bytes):
+    """Bytes the method must move: K and V of every visible position once per
+    GQA group, q read and out written once, the page ids of the pages used,
+    the lengths and query offsets.  (Page "32. Production attention kernels",
+    What the reference backend costs: 2 x Hkv x D values per token per layer.)"""
+    kv = sum(max(0, L) for L in context_lens) * num_kv_heads * head_dim * 2 * elem_bytes
+    n = sum(query_lens)
+    qo = n * num_q_heads * head_dim * elem_bytes * 2
+    ids = sum((max(0, L) + page_size - 1) // page_size for L in context_lens) * 4
+    meta = (2 * len(context_lens) + 1) * 4
+    return kv + qo + ids + meta
+
+
+def algorithmic_flops(context_lens, query_lens, num_q_heads, head_dim, causal=True):
+    """4 * D * Hq per visible (query, key) pair: 2 for q.k and 2 for p.v."""
+    pairs = 0
+    for L, n in zip(context_lens, query_lens):
+        for t in range(n):
+            pos = L - n + t
+            pairs += max(0, min(L, pos + 1)) if causal else L
+    return 4 * head_dim * num_q_heads * pairs
+
+
+def kv_write_bytes(tokens, num_kv_heads, head_dim, elem_bytes):
+    return 2 * 2 * tokens * num_kv_heads * head_dim * elem_bytes + 4 * tokens
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- GPU workloads
+class DecodeBench:
+    """Headline decode workload with rotated pool sets."""
+
+    def __init__(self, layers=4, num_splits=0):
+        import torch
+        import paged_kv_attention_amd as pa
+        from workloads import make
+        self.torch, self.pa = torch, pa
+        self.w = make(3)
+        dev = torch.device("cuda", 0)
+        w = self.w
+        self.q = w.q.to(dev)
+        self.bt = w.block_tables.to(dev)
+        self.cl = w.context_lens.to(dev)
+        self.qsl = w.query_start_loc.to(dev)
+        self.pools = [(w.k_pool.to(dev), w.v_pool.to(dev))]
+        gen = torch.Generator(device=dev).manual_seed(1234)
+        for _ in range(layers - 1):
+            k = torch.randn(w.k_pool.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            v = torch.randn(w.v_pool.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            self.pools.append((k, v))
+        self.out = torch.empty_like(self.q)
+        self.dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=1,
+                                 num_splits=num_splits)
+        ws = pa.workspace_size(self.dims, torch.bfloat16)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.splits = pa.choose_splits(self.dims)
+        self.num_splits = num_splits
+        # the step's new token of each sequence sits at its newest position L-1
+        lens = w.context_lens.tolist()
+        ps = w.page_size
+        slots = [int(w.block_tables[b, (L - 1) // ps]) * ps + (L - 1) % ps for b, L in enumerate(lens)]
+        self.slots = torch.tensor(slots, dtype=torch.int32, device=dev)
+        self.k_new = torch.randn(len(lens), w.num_kv_heads, w.head_dim, generator=gen, device=dev).to(torch.bfloat16)
+        self.v_new = torch.randn(len(lens), w.num_kv_heads, w.head_dim, generator=gen, device=dev).to(torch.bfloat16)
+        self.attn_bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, ps, 2)
+        self.write_bytes = kv_write_bytes(len(lens), w.num_kv_heads, w.head_dim, 2)
+
+    def attend(self, layer):
+        k, v = self.pools[layer % len(self.pools)]
+        return self.pa.paged_attention(self.q, k, v, self.bt, self.cl, self.qsl, self.w.scale, True, out=self.out,
+                                       workspace=self.ws, max_query_len=1, num_splits=self.num_splits)
+
+    def write(self, layer):
+        k, v = self.pools[layer % len(self.pools)]
+        self.pa.kv_cache_write(self.k_new, self.v_new, k, v, self.slots)
+
+    def parity(self, seqs=(0, 17, 63)):
+        """Sampled check of layer 0 against the oracle, before any write."""
+        from oracle import attention_f64
+        torch = self.torch
+        out = self.attend(0).cpu()
+        toks = list(seqs)
+        w = self.w
+        ref = attention_f64(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
+                            tokens=toks)
+        idx = torch.tensor(toks)
+        return torch.max(torch.abs(out.index_select(0, idx).double() - ref.index_select(0, idx))).item()
+
+
+class PrefillBench:
+    def __init__(self, config=5):
+        import torch
+        import paged_kv_attention_amd as pa
+        from workloads import make
+        self.torch, self.pa = torch, pa
+        self.w = w = make(config)
+        dev = torch.device("cuda", 0)
+        self.q = w.q.to(dev)
+        self.k, self.v = w.k_pool.to(dev), w.v_pool.to(dev)
+        self.bt = w.block_tables.to(dev)
+        self.cl = w.context_lens.to(dev)
+        self.qsl = w.query_start_loc.to(dev)
+        self.out = torch.empty_like(self.q)
+        self.mql = w.max_query_len
+        lens = w.context_lens.tolist()
+        ps = w.page_size
+        # the prompt's K/V rows are written through the slot map in the same step
+        slots = []
+        for b, L in enumerate(lens):
+            for j in range(L):
+                slots.append(int(w.block_tables[b, j // ps]) * ps + j % ps)
+        self.slots = torch.tensor(slots, dtype=torch.int32, device=dev)
+        gen = torch.Generator(device=dev).manual_seed(99)
+        T = len(slots)
+        self.k_new = torch.randn(T, w.num_kv_heads, w.head_dim, generator=gen, device=dev).to(torch.bfloat16)
+        self.v_new = torch.randn(T, w.num_kv_heads, w.head_dim, generator=gen, device=dev).to(torch.bfloat16)
+        self.flops = algorithmic_flops(lens, w.query_lens, w.num_q_heads, w.head_dim)
+
+    def write(self):
+        self.pa.kv_cache_write(self.k_new, self.v_new, self.k, self.v, self.slots)
+
+    def attend(self):
+        return self.pa.paged_attention(self.q, self.k, self.v, self.bt, self.cl, self.qsl, self.w.scale, True,
+                                       out=self.out, max_query_len=self.mql)
+
+
+def _time_steps(step_fns, steps, warmup):
+    """Run warmup, then time `steps` steps; each fn in step_fns is timed with
+    HIP events on the current stream.  Returns (total_ms, [avg ms per fn])."""
+    import torch
+    for i in range(warmup):
+        for f in step_fns:
+            f(i)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in step_fns]
+           for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        for j, f in enumerate(step_fns):
+            evs[i][j][0].record()
+            f(warmup + i)
+            evs[i][j][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)) / steps for j in range(len(step_fns))]
+    return total, per
+
+
+def cpu_baseline(w, seconds_target=12.0):
+    """The float64 oracle, as it stands, on a bounded sample of the decode
+    workload: whole sequences (all heads) in order, cycling, until about
+    `seconds_target` seconds of host work are done."""
+    import torch
+    from oracle import attention_f64
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    qsl = w.query_start_loc.tolist()
+    lens = w.context_lens.tolist()
+    done_seqs, done_bytes = 0, 0
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < seconds_target:
+        b = done_seqs % w.num_seqs
+        sub_qsl = torch.tensor([0, qsl[b + 1] - qsl[b]], dtype=torch.int32)
+        attention_f64(w.q[qsl[b]:qsl[b + 1]], w.k_pool, w.v_pool, w.block_tables[b:b + 1],
+                      w.context_lens[b:b + 1], sub_qsl, w.scale)
+        done_bytes += algorithmic_bytes([lens[b]], [qsl[b + 1] - qsl[b]], w.num_q_heads, w.num_kv_heads,
+                                        w.head_dim, w.page_size, 2)
+        done_seqs += 1
+    el = time.perf_counter() - t_start
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{done_seqs} sequence passes (64 x 4096 decode step, one sequence with all 32 heads "
+                      f"per pass), float64, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="time one workload only (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (scales profiler byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design note, "
+              "not a built path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import paged_kv_attention_amd as pa
+    pa.load_library()
+    result = {}
+    decode_w = None
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 1 GiB device copy done", file=sys.stderr, flush=True)
+
+    if args.only in (None, "decode"):
+        print("[bench] decode: building inputs", file=sys.stderr, flush=True)
+        db = DecodeBench(layers=args.layers, num_splits=args.num_splits)
+        err = db.parity()
+        print(f"[bench] decode parity (3 sampled sequences): max abs err {err:.3e}", file=sys.stderr, flush=True)
+        total, per = _time_steps([db.write, db.attend], args.steps, args.warmup)
+        ms = total / args.steps
+        value = db.attn_bytes / (ms * 1e-3) / 1e9
+        kern_ms = per[1]
+        achieved = db.attn_bytes / (kern_ms * 1e-3) / 1e9
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("decode_src_sha256_16") == _src_hash(DECODE_KERNEL_SRC):
+                traffic = tr.get("bytes_per_launch")
+        result.update({
+            "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "decode step: 64 seqs x 4096 ctx, 32 q / 8 kv heads, head_dim 128, page 64, "
+                                   "bf16; kv_cache_write of 64 new tokens + paged_attention",
+                       "seqs": 64, "context": 4096, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
+                       "page_size": 64, "splits": db.splits, "pool_sets_rotated": args.layers,
+                       "algorithmic_bytes_per_step": db.attn_bytes},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "kernel": "decode_splitkv_kernel<128,1>", "kernel_ms": round(kern_ms, 5),
+                         "bytes_per_launch": db.attn_bytes},
+            "kv_write_ms": round(per[0], 5),
+            "parity_max_abs_err": err,
+        })
+        decode_w = db.w
+        del db
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "prefill") and not args.no_prefill:
+        print("[bench] prefill: building inputs", file=sys.stderr, flush=True)
+        pb = PrefillBench(5)
+        psteps = max(3, min(args.steps, 10))
+        total, per = _time_steps([lambda i: pb.write(), lambda i: pb.attend()], psteps, max(1, min(args.warmup, 3)))
+        kern_ms = per[1]
+        step_ms = total / psteps
+        tflops_kernel = pb.flops / (kern_ms * 1e-3) / 1e12
+        tflops_step = pb.flops / (step_ms * 1e-3) / 1e12
+        pre = {"workload": "causal prefill 4 x 8192, 32 q / 8 kv heads, head_dim 128, page 64, bf16; "
+                           "kv_cache_write of 32768 tokens + paged_attention",
+               "steps": psteps, "ms_per_step": round(step_ms, 4), "tflops_step": round(tflops_step, 2),
+               "algorithmic_flops": pb.flops,
+               "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tflops_kernel / BF16_PEAK_TFLOPS, 4),
+                            "traffic": None, "kernel": "prefill_kernel<128>", "kernel_ms": round(kern_ms, 4)}}
+        if args.only == "prefill":
+            result.update({"metric": METRIC, "value": round(tflops_kernel, 2), "unit": "TFLOP/s", "n_gpus": 1,
+                           "steps": psteps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+                           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                           "data": "synthetic", "config": {"workload": pre["workload"]},
+                           "roofline": pre["roofline"]})
+        else:
+            result["prefill"] = pre
+        del pb
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline and args.only is None and decode_w is not None:
+        print("[bench] cpu baseline: timing the float64 oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(decode_w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,90 @@
+// Host unit test of the planning and validation code (built with g++ and
+// AddressSanitizer by tests/test_host_logic.py; no GPU involved).
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "host_logic.h"
+
+static int failures = 0;
+#define CHECK(c) do { if (!(c)) { std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #c); ++failures; } } while (0)
+
+static pa_dims dims(int B, int N, int mql, int Hq, int Hkv, int D, int ps, int P, int W) {
+  pa_dims d{};
+  d.num_seqs = B; d.num_tokens = N; d.max_query_len = mql; d.num_q_heads = Hq; d.num_kv_heads = Hkv;
+  d.head_dim = D; d.page_size = ps; d.num_pages = P; d.table_width = W;
+  d.q_stride_tok = (int64_t)Hq * D; d.q_stride_head = D; d.o_stride_tok = (int64_t)Hq * D; d.o_stride_head = D;
+  d.kv_stride_page = (int64_t)ps * Hkv * D; d.kv_stride_slot = (int64_t)Hkv * D; d.kv_stride_head = D;
+  return d;
+}
+
+int main() {
+  // decode 64 x 4096: one split fills 256 CUs twice over
+  pa_dims c3 = dims(64, 64, 1, 32, 8, 128, 64, 4096, 64);
+  CHECK(pa::check_dims(&c3, PA_BF16) == PA_OK);
+  pa::Plan p3 = pa::make_plan(&c3, PA_BF16, 256);
+  CHECK(p3.splits == 1 && p3.workspace_bytes == 0 && p3.dec_small && !p3.dec_big && !p3.prefill && !p3.combine);
+  // ragged 32 sequences: two splits, workspace for every row
+  pa_dims c2 = dims(32, 32, 1, 32, 8, 128, 64, 2000, 64);
+  pa::Plan p2 = pa::make_plan(&c2, PA_BF16, 256);
+  CHECK(p2.splits == 2 && p2.pages_per_split == 32 && p2.combine && p2.comb_tokens == 1);
+  CHECK(p2.workspace_bytes == (size_t)2 * 32 * 32 * 130 * 4);
+  // mixed batch: prefill + small and large decode tiles
+  pa_dims c4 = dims(32, 547, 512, 32, 8, 128, 64, 2000, 128);
+  pa::Plan p4 = pa::make_plan(&c4, PA_BF16, 256);
+  CHECK(p4.prefill && p4.tok_per_tile == 32 && p4.num_qtiles == 16 && p4.dec_small && p4.dec_big && p4.big_nt == 4);
+  CHECK(p4.dec_max_n == 16 && p4.comb_max_n == 16);
+  // a 5-token verify bound: 20 rows -> 32-row tile
+  pa_dims v5 = dims(4, 20, 5, 32, 8, 128, 64, 100, 16);
+  pa::Plan pv = pa::make_plan(&v5, PA_BF16, 256);
+  CHECK(!pv.prefill && pv.dec_small && pv.dec_big && pv.big_nt == 2);
+  // group 32: even one token needs 32 rows; decode class stops at 2 tokens
+  pa_dims g32 = dims(2, 2, 1, 64, 2, 128, 64, 100, 16);
+  pa::Plan pg = pa::make_plan(&g32, PA_BF16, 256);
+  CHECK(pg.dec_max_n == 2 && !pg.dec_small && pg.dec_big && pg.big_nt == 2);
+  // float32: one combine over every token when split
+  pa_dims c1 = dims(1, 1, 1, 8, 2, 64, 16, 64, 38);
+  pa::Plan p1 = pa::make_plan(&c1, PA_F32, 256);
+  CHECK(p1.splits == 3 && p1.pages_per_split == 13 && p1.combine && p1.comb_tokens == 1);
+  c1.num_splits = 38;
+  CHECK(pa::make_plan(&c1, PA_F32, 256).splits == 38);
+  c1.num_splits = 100;
+  CHECK(pa::choose_splits(&c1, PA_F32, 256) == 38);
+  // argument checks
+  pa_dims bad = c3; bad.num_kv_heads = 3;
+  CHECK(pa::check_dims(&bad, PA_BF16) == PA_ERR_SHAPE);
+  bad = c3; bad.head_dim = 96;
+  CHECK(pa::check_dims(&bad, PA_BF16) == PA_ERR_UNSUPPORTED);
+  bad = c3; bad.kv_stride_slot = 1028;
+  CHECK(pa::check_dims(&bad, PA_BF16) == PA_ERR_UNSUPPORTED);
+  CHECK(pa::check_dims(&bad, PA_F32) == PA_OK);     // 4-element multiple suffices for float32
+  bad = c3; bad.q_stride_head = 64;
+  CHECK(pa::check_dims(&bad, PA_BF16) == PA_ERR_SHAPE);
+  CHECK(pa::check_dims(nullptr, PA_BF16) == PA_ERR_NULL);
+
+  // validate_host
+  pa_dims v = dims(2, 3, 0, 4, 2, 64, 16, 4, 2);
+  std::vector<int32_t> bt = {0, 1, 2, 3}, lens = {20, 5}, qsl = {0, 2, 3}, slots = {5, -1, 63};
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), slots.data(), 3, 1, &v) == PA_OK);
+  lens[0] = 33;   // beyond W * ps
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 1, &v) == PA_ERR_INVALID_DATA);
+  lens[0] = 20; bt[1] = 4;  // page outside the pool
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 1, &v) == PA_ERR_INVALID_DATA);
+  bt[1] = 1; bt[3] = 77;    // unused entry: not checked
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 1, &v) == PA_OK);
+  qsl = {0, 3, 2};
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 1, &v) == PA_ERR_INVALID_DATA);
+  qsl = {0, 2, 3}; lens[1] = 0;   // one token over an empty context under causal
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 1, &v) == PA_ERR_INVALID_DATA);
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 0, &v) == PA_OK);
+  lens[1] = 5; slots = {5, 5, -1};
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), slots.data(), 3, 1, &v) == PA_ERR_INVALID_DATA);
+  slots = {64, -1, 0};
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), slots.data(), 3, 1, &v) == PA_ERR_INVALID_DATA);
+  slots = {-2, -1, 0};
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), slots.data(), 3, 1, &v) == PA_ERR_INVALID_DATA);
+
+  if (failures) { std::printf("%d failures\n", failures); return 1; }
+  std::printf("host logic: all checks passed\n");
+  return 0;
+}

@@ -1,0 +1,100 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol the
+header declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_amd as pa
+from paged_kv_attention_amd._lib import PaDims
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w ]*?[\s\*]+)?([A-Za-z_]\w*)\s*\(", text, flags=re.M))
+                  - {"if", "defined"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.load_library()
+    declared = _declared_functions()
+    assert set(pa.EXPORTED) == set(declared), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert pa.status_string(pa.PA_OK) == "ok"
+    for s in range(1, 7):
+        assert pa.status_string(s) and pa.status_string(s) != "unknown status"
+    assert pa.status_string(99) == "unknown status"
+
+
+def _dims(**kw):
+    d = PaDims()
+    base = dict(num_seqs=2, num_tokens=2, max_query_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                page_size=64, num_pages=128, table_width=64, num_splits=0, q_stride_tok=32 * 128,
+                q_stride_head=128, o_stride_tok=32 * 128, o_stride_head=128, kv_stride_page=64 * 8 * 128,
+                kv_stride_slot=8 * 128, kv_stride_head=128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def _call(d, dtype=1, scale=0.088, ptr=None, ws=None, ws_bytes=0):
+    lib = pa.load_library()
+    p = ptr
+    return lib.paged_attention(p, p, p, p, p, p, ctypes.c_float(scale), 1, p, ws, ws_bytes, ctypes.byref(d), dtype,
+                               None)
+
+
+def test_argument_errors_return_status_without_launch():
+    lib = pa.load_library()
+    assert lib.paged_attention(None, None, None, None, None, None, 1.0, 1, None, None, 0, None, 1, None) == pa.PA_ERR_NULL
+    assert _call(_dims(num_kv_heads=3)) == pa.PA_ERR_SHAPE                 # 32 % 3 != 0
+    assert _call(_dims(head_dim=96)) == pa.PA_ERR_UNSUPPORTED
+    assert _call(_dims(page_size=8)) == pa.PA_ERR_UNSUPPORTED
+    assert _call(_dims(), dtype=7) == pa.PA_ERR_UNSUPPORTED
+    assert _call(_dims(q_stride_head=100)) == pa.PA_ERR_SHAPE              # rows overlap: D not contiguous
+    assert _call(_dims(kv_stride_slot=8 * 128 + 3)) == pa.PA_ERR_UNSUPPORTED   # breaks 16-byte loads
+    assert _call(_dims(num_seqs=-1)) == pa.PA_ERR_SHAPE
+    assert _call(_dims(), scale=float("nan")) == pa.PA_ERR_SHAPE
+    assert _call(_dims()) == pa.PA_ERR_NULL                                 # valid dims, NULL buffers
+    assert _call(_dims(num_seqs=0, num_tokens=0)) == pa.PA_OK              # nothing to do
+    assert _call(_dims(num_q_heads=65 * 2, num_kv_heads=2, q_stride_tok=130 * 128, o_stride_tok=130 * 128)) \
+        == pa.PA_ERR_UNSUPPORTED                                            # bf16 group > 64
+
+
+def test_workspace_and_split_rules():
+    lib = pa.load_library()
+    # 64 x 8 (sequence, KV head) units already fill 2 workgroups per CU: one split, no workspace
+    d = _dims(num_seqs=64, num_tokens=64)
+    assert lib.pa_choose_splits(ctypes.byref(d)) == 1
+    assert lib.pa_workspace_size(ctypes.byref(d), 1) == 0
+    # 32 sequences: two splits
+    d = _dims(num_seqs=32, num_tokens=32)
+    cus = lib.pa_device_cu_count()
+    S = lib.pa_choose_splits(ctypes.byref(d))
+    assert S == min(32, -(-2 * cus // (32 * 8)), 64 // 4)
+    assert lib.pa_workspace_size(ctypes.byref(d), 1) == (S * 32 * 32 * 130 * 4 if S > 1 else 0)
+    # an explicit count wins (capped at the table width)
+    d = _dims(num_splits=3)
+    assert lib.pa_choose_splits(ctypes.byref(d)) == 3
+    assert lib.pa_workspace_size(ctypes.byref(d), 1) == 3 * 2 * 32 * 130 * 4
+    d = _dims(num_splits=500)
+    assert lib.pa_choose_splits(ctypes.byref(d)) == 64
+
+
+def test_kv_write_argument_errors():
+    lib = pa.load_library()
+    d = _dims()
+    assert lib.kv_cache_write(None, None, None, None, None, 4, 1024, 128, ctypes.byref(d), 1, None) == pa.PA_ERR_NULL
+    assert lib.kv_cache_write(None, None, None, None, None, 0, 1024, 128, ctypes.byref(d), 1, None) == pa.PA_OK
+    assert lib.kv_cache_write(None, None, None, None, None, 4, 1024, 128, None, 1, None) == pa.PA_ERR_NULL
+    assert lib.kv_cache_write(None, None, None, None, None, 4, 1024, 128, ctypes.byref(_dims(head_dim=80)), 1,
+                              None) == pa.PA_ERR_UNSUPPORTED
