@@ -88,11 +88,14 @@ class DecodeBench:
         self.bt = w.block_tables.to(dev)
         self.cl = w.context_lens.to(dev)
         self.qsl = w.query_start_loc.to(dev)
-        self.pools = [(w.k_pool.to(dev), w.v_pool.to(dev))]
+        self.pools = [(pa.pool_like(w.k_pool, dev), pa.pool_like(w.v_pool, dev))]
         gen = torch.Generator(device=dev).manual_seed(1234)
+        P, ps, Hkv, D = w.k_pool.shape
         for _ in range(layers - 1):
-            k = torch.randn(w.k_pool.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-            v = torch.randn(w.v_pool.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            k = pa.empty_pool(P, ps, Hkv, D, device=dev)
+            v = pa.empty_pool(P, ps, Hkv, D, device=dev)
+            k.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
+            v.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
             self.pools.append((k, v))
         self.out = torch.empty_like(self.q)
         self.dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=1,
@@ -142,7 +145,7 @@ class PrefillBench:
         self.w = w = make(config)
         dev = torch.device("cuda", 0)
         self.q = w.q.to(dev)
-        self.k, self.v = w.k_pool.to(dev), w.v_pool.to(dev)
+        self.k, self.v = pa.pool_like(w.k_pool, dev), pa.pool_like(w.v_pool, dev)
         self.bt = w.block_tables.to(dev)
         self.cl = w.context_lens.to(dev)
         self.qsl = w.query_start_loc.to(dev)
@@ -282,6 +285,7 @@ def main():
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "decode step: 64 seqs x 4096 ctx, 32 q / 8 kv heads, head_dim 128, page 64, "
                                    "bf16; kv_cache_write of 64 new tokens + paged_attention",
+                       "pool_layout": "head-major pages [P, Hkv, ps, D]",
                        "seqs": 64, "context": 4096, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
                        "page_size": 64, "splits": db.splits, "pool_sets_rotated": args.layers,
                        "algorithmic_bytes_per_step": db.attn_bytes},

@@ -117,6 +117,30 @@ def make_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor,
     return d
 
 
+def empty_pool(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int, dtype=torch.bfloat16,
+               device="cuda", layout: str = "head_major") -> torch.Tensor:
+    """Allocate one K or V pool and return it as a ``[P, ps, Hkv, D]`` view.
+
+    ``layout="head_major"`` stores each page as ``Hkv`` dense ``[ps, D]`` tiles
+    (``[P, Hkv, ps, D]`` in memory), so one (page, KV head) is one contiguous
+    run of ``ps * D`` elements; this is the layout the decode kernel reads
+    fastest.  ``layout="interleaved"`` stores ``[P, ps, Hkv, D]`` as is.
+    """
+    if layout == "head_major":
+        return torch.empty(num_pages, num_kv_heads, page_size, head_dim, dtype=dtype, device=device).permute(0, 2, 1, 3)
+    if layout == "interleaved":
+        return torch.empty(num_pages, page_size, num_kv_heads, head_dim, dtype=dtype, device=device)
+    raise ValueError(f"unknown pool layout {layout!r}")
+
+
+def pool_like(pool: torch.Tensor, device="cuda", layout: str = "head_major") -> torch.Tensor:
+    """Copy a logical ``[P, ps, Hkv, D]`` pool into device memory in the given layout."""
+    out = empty_pool(*pool.shape[:1], pool.shape[1], pool.shape[2], pool.shape[3], dtype=pool.dtype, device=device,
+                     layout=layout)
+    out.copy_(pool)
+    return out
+
+
 def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype != torch.int32:
         raise TypeError(f"{name} must be int32 (convert int64 metadata once, outside timed regions)")

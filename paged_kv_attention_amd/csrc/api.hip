@@ -106,6 +106,7 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
   p.group = Hq / dims->num_kv_heads;
   p.head_dim = dims->head_dim;
   p.page_size = dims->page_size;
+  p.page_shift = __builtin_ctz((unsigned)dims->page_size);
   p.num_pages = dims->num_pages;
   p.table_width = dims->table_width;
   p.num_splits = pl.splits;

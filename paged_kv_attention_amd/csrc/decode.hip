@@ -8,9 +8,8 @@
 // Production attention kernels", One kernel for the whole batch).
 //
 // The split's keys are cut into 32-key chunks; wave w walks chunks w, w+4,
-// ... with its own online-softmax state (running max m, sum l, accumulator),
-// prefetching its next chunk's K and V into registers while it computes the
-// current one.  Per chunk:
+// ... with its own online-softmax state (running max m, sum l, accumulator):
+// it loads a chunk's K and V into registers, then computes it.  Per chunk:
 //   S^T[32 keys x rows] = K . Q^T   on v_mfma_f32_16x16x32_bf16, K loaded
 //                                   from the page straight into the A operand
 //                                   (8 contiguous dims per lane);
@@ -48,6 +47,7 @@ struct DecodeCfg {
   static constexpr int ROW_BYTES = D * 2 + 32;   // V staging row stride (32 B pad: no bank conflicts
                                                  // between the 4 rows a transpose read touches)
   static constexpr int WAVE_LDS = KC * ROW_BYTES;
+  static constexpr int NBUF = 1;                 // register chunks per wave (see the main loop)
 };
 
 template <int D, int NT>
@@ -66,7 +66,7 @@ struct DecodeChunk {
 };
 
 template <int D, int NT>
-__global__ __launch_bounds__(256) void decode_splitkv_kernel(const AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D>;
   constexpr int ROWS = 16 * NT;
   constexpr int ORS = DecodeLds<D, NT>::ORS;
@@ -230,21 +230,22 @@ __global__ __launch_bounds__(256) void decode_splitkv_kernel(const AttnParams p)
     }
   };
 
-  int c = wave;
-  if (c < nchunks) {
-    DecodeChunk<D> ca, cb;
-    load(c, ca);
-    while (true) {
-      const bool hb = c + 4 < nchunks;
-      if (hb) load(c + 4, cb);
-      process(c, ca);
-      c += 4;
-      if (!hb) break;
-      const bool ha = c + 4 < nchunks;
-      if (ha) load(c + 4, ca);
-      process(c, cb);
-      c += 4;
-      if (!ha) break;
+  // Register pipeline of NBUF chunks per wave: chunk c + 4*(NBUF-1) is loaded
+  // while chunk c is computed.  NBUF = 1 (load a chunk, then compute it) is
+  // the measured best on the 64 x 4096 decode step: a second chunk in flight
+  // per wave (register double buffering, or issuing the next chunk's loads
+  // before this chunk's softmax) lowers the achieved HBM bandwidth.
+  DecodeChunk<D> buf[C::NBUF];
+#pragma unroll
+  for (int j = 0; j < C::NBUF - 1; ++j)
+    if (wave + 4 * j < nchunks) load(wave + 4 * j, buf[j]);
+  for (int base = wave; base < nchunks; base += 4 * C::NBUF) {
+#pragma unroll
+    for (int k = 0; k < C::NBUF; ++k) {
+      const int c = base + 4 * k;
+      const int cn = c + 4 * (C::NBUF - 1);
+      if (cn < nchunks) load(cn, buf[(k + C::NBUF - 1) % C::NBUF]);
+      if (c < nchunks) process(c, buf[k]);
     }
   }
 

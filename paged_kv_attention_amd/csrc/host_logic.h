@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/pagedattn.h"
+#include "pagedattn.h"
 
 namespace pa {
 

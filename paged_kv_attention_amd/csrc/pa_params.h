@@ -23,7 +23,7 @@ struct AttnParams {
   int64_t kv_stride_page, kv_stride_slot, kv_stride_head;
   float scale_log2;         // scale * log2(e): scores go straight into exp2
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, group;
-  int32_t head_dim, page_size, num_pages, table_width;
+  int32_t head_dim, page_size, page_shift, num_pages, table_width;
   int32_t num_splits;       // S (>= 1)
   int32_t pages_per_split;  // ceil(W / S)
   int32_t causal;

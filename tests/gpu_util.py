@@ -14,20 +14,18 @@ from workloads import Workload
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
 
 
-def to_dev(w: Workload, layout: str = "default"):
+def to_dev(w: Workload, layout: str = "head_major"):
+    """Device copies of a workload; pools in the given physical layout
+    ("head_major": [P, Hkv, ps, D] storage, "interleaved": [P, ps, Hkv, D]),
+    always passed as [P, ps, Hkv, D] views."""
     dev = torch.device("cuda", 0)
-    k, v = w.k_pool, w.v_pool
-    if layout == "head_major":
-        # store each page head-major ([P, Hkv, ps, D]) and pass a [P, ps, Hkv, D] strided view
-        k = k.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
-        v = v.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
-    else:
-        k, v = k.to(dev), v.to(dev)
+    k = pa.pool_like(w.k_pool, dev, layout)
+    v = pa.pool_like(w.v_pool, dev, layout)
     return dict(q=w.q.to(dev), k_pool=k, v_pool=v, block_tables=w.block_tables.to(dev),
                 context_lens=w.context_lens.to(dev), query_start_loc=w.query_start_loc.to(dev))
 
 
-def run_lib(w: Workload, num_splits: int = 0, layout: str = "default", max_query_len: Optional[int] = None,
+def run_lib(w: Workload, num_splits: int = 0, layout: str = "head_major", max_query_len: Optional[int] = None,
             out_fill: Optional[float] = None) -> torch.Tensor:
     t = to_dev(w, layout)
     out = None

@@ -154,11 +154,29 @@ def test_repeated_launch_is_bitwise_identical():
     assert torch.equal(run_lib(w), run_lib(w))
 
 
-def test_head_major_pool_layout_via_strides():
+def test_interleaved_pool_layout_via_strides():
+    """The [P, ps, Hkv, D] storage of the pages' interface runs through the same kernels."""
     w = poison_unused(_custom(130, [500, 65, 300], [1, 5, 100], Hq=8, Hkv=2))
-    check(w, run_lib(w, layout="head_major"), label="bf16 head-major pool")
+    check(w, run_lib(w, layout="interleaved"), label="bf16 interleaved pool")
     w = poison_unused(_custom(131, [500, 65], [1, 5], Hq=8, Hkv=2, D=64, ps=16, dtype=torch.float32))
-    check(w, run_lib(w, layout="head_major"), label="fp32 head-major pool")
+    check(w, run_lib(w, layout="interleaved"), label="fp32 interleaved pool")
+    w = poison_unused(make(2))
+    check(w, run_lib(w, layout="interleaved"), label="C2 interleaved pool")
+
+
+def test_kv_write_head_major_pool():
+    w = _custom(132, [300], [1], Hq=8, Hkv=2)
+    dev = torch.device("cuda", 0)
+    kd = pa.pool_like(w.k_pool, dev, "head_major")
+    vd = pa.pool_like(w.v_pool, dev, "head_major")
+    g = torch.Generator().manual_seed(4)
+    k_new = torch.randn(5, 2, 128, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(5, 2, 128, generator=g).to(torch.bfloat16)
+    slots = torch.tensor([7, 64, -1, 129, 3], dtype=torch.int32)
+    pa.kv_cache_write(k_new.to(dev), v_new.to(dev), kd, vd, slots.to(dev))
+    torch.cuda.synchronize()
+    ek, ev = kv_write_ref(k_new, v_new, w.k_pool, w.v_pool, slots)
+    assert torch.equal(kd.cpu(), ek) and torch.equal(vd.cpu(), ev)
 
 
 def test_length_beyond_table_is_clamped():
