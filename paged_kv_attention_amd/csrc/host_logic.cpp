@@ -1,5 +1,6 @@
 // Host-only planning for paged_attention (see host_logic.h).
 #include "host_logic.h"
+#include "pa_params.h"
 
 #include <limits.h>
 
@@ -82,7 +83,7 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count) {
     pl.dec_big = dmax * G > 16;
     pl.big_nt = dmax * G <= 32 ? 2 : 4;
     pl.prefill = pl.mql > pl.dec_max_n;
-    pl.tok_per_tile = 128 / G;
+    pl.tok_per_tile = prefill_tile_rows(d->head_dim) / G;
     pl.num_qtiles = pl.prefill ? (pl.mql + pl.tok_per_tile - 1) / pl.tok_per_tile : 0;
     pl.combine = pl.splits > 1 && dmax >= 1;
     pl.comb_tokens = dmax;

@@ -19,7 +19,7 @@ struct Plan {
   bool dec_big;            // bf16: decode launch for 16 < n*G <= 16*big_nt
   int big_nt;              // 2 or 4 row tiles
   bool prefill;            // bf16: prefill launch for n > dec_max_n
-  int tok_per_tile;        // prefill: tokens per 128-row tile
+  int tok_per_tile;        // prefill: tokens per tile (tile rows / G)
   int num_qtiles;          // prefill: tiles per sequence (from mql)
   bool combine;            // split partials need the combine launch
   int comb_tokens;         // combine: token slots per sequence

@@ -8,6 +8,10 @@
 
 namespace pa {
 
+// Query rows per prefill workgroup tile (32 per wave): 8 waves for head_dim
+// <= 128, 4 waves for 256 (its accumulator does not fit two waves per SIMD).
+constexpr int prefill_tile_rows(int head_dim) { return head_dim <= 128 ? 256 : 128; }
+
 struct AttnParams {
   const void* q;
   const void* k_pool;

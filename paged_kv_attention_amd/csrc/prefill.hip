@@ -1,26 +1,32 @@
 // Prefill-chunk attention for gfx950 (bf16 Q/K/V, MFMA 32x32x16).
 //
-// A workgroup of 4 waves owns one tile of 128 query rows of one sequence and
-// one KV head g.  Rows are GQA-packed like the decode tile: row r of the tile
-// is token t0 + r / G and query head g*G + r % G, so a K/V block staged in
-// LDS serves all G heads of the group (page "Attention kernels", Open
+// A workgroup of NW waves owns one tile of 32*NW query rows of one sequence
+// and one KV head g.  Rows are GQA-packed like the decode tile: row r of the
+// tile is token t0 + r / G and query head g*G + r % G, so a K/V block staged
+// in LDS serves all G heads of the group (page "Attention kernels", Open
 // questions: GQA packing in the prefill kernel; page "32. Production attention
 // kernels", One kernel for the whole batch).  Each wave owns 32 rows.
 //
-// The tile walks the sequence's pages in 64-key blocks, stopping at the key
-// its last token can see (same page, "The key loop stops at the tile's last
-// query").  Blocks are staged through a double-buffered LDS ring: the next
-// block's K and V are fetched into registers while the current block is
-// computed.  Per block and wave:
+// The tile walks the sequence's pages in 64-key blocks and stops at the key
+// its last token can see (page "32. Production attention kernels": the key
+// loop stops at the tile's last query).  Blocks pass through a two-stage LDS
+// ring; each thread also holds up to PF further blocks in registers, so a
+// block's global loads are issued PF block-computes before they are needed.
+// Per block and wave:
 //   S^T[64 keys x 32 rows] = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS);
 //   mask only blocks that reach the diagonal or the context end (page
 //   "Attention kernels", Walking the block table: only pages that overlap the
 //   diagonal are masked);
-//   online softmax in float32 with exp2 (scale*log2 e folded in);
-//   P rounded to bf16, O^T[D x 32 rows] += V^T . P^T on MFMA, V^T read
-//   transposed from LDS (ds_read_b64_tr_b16), P^T taken straight from the
-//   S^T accumulator registers.
-// Keys past the context end are zero-filled in LDS, never loaded.
+//   online softmax in float32 with exp2; the scale*log2(e) factor and the
+//   running max meet in one FMA per score (page "Attention kernels", One
+//   kernel family).  The reference max of a row only moves when a block's max
+//   exceeds it by more than 8 (log2 units): probabilities then stay below 2^8,
+//   and since the row sum uses the same reference the normalised result is
+//   the same softmax, while most blocks skip the accumulator rescale;
+//   P rounded to bf16 (same passage), its row sum taken from the rounded
+//   values, O^T[D x 32 rows] += V^T . P^T on MFMA with V^T read transposed from
+//   LDS (ds_read_b64_tr_b16) and P^T taken straight from the S^T accumulator.
+// Keys past the context end are zero-filled in LDS and never loaded.
 //
 // Tiles with more keys run first (page "Attention kernels", Open questions:
 // heaviest causal blocks first), and the flat block index is remapped so
@@ -30,24 +36,32 @@
 
 namespace pa {
 
-template <int D>
+template <int D, int NW, int PF>
 struct PrefillCfg {
-  static constexpr int BM = 128;                 // rows per workgroup (4 waves x 32)
+  static constexpr int NTH = 64 * NW;            // threads per workgroup
+  static constexpr int BM = 32 * NW;             // rows per workgroup
   static constexpr int KB = 64;                  // keys per block
   static constexpr int DS = D / 16;              // k-steps of QK^T
   static constexpr int DT = D / 32;              // 32-dim output tiles
   static constexpr int CPL = D / 8;              // 16-byte chunks per key row
-  static constexpr int LOADS = KB * CPL / 256;   // 16-byte loads per thread per tensor
+  static constexpr int LOADS = KB * CPL / NTH;   // 16-byte loads per thread per tensor
   static constexpr int KRS = D * 2 + 16;         // K row stride (bytes)
   static constexpr int VRS = D * 2 + 32;         // V row stride (bytes)
   static constexpr int KBYTES = KB * KRS;
   static constexpr int STAGE = KBYTES + KB * VRS;
   static constexpr int LDS = 2 * STAGE;
+  static constexpr float TAU = 8.f;              // lazy-rescale threshold (log2 units)
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
-  using C = PrefillCfg<D>;
+template <int D, int NW>
+struct PrefillRegs {
+  u32x4 k[PrefillCfg<D, NW, 1>::LOADS], v[PrefillCfg<D, NW, 1>::LOADS];
+};
+
+template <int D, int NW, int PF>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void prefill_kernel(const AttnParams p) {
+  using C = PrefillCfg<D, NW, PF>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   // ---- XCD-aware block order: consecutive logical tiles share an XCD
@@ -71,7 +85,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
   const int tcount = min(TPT, n - t0);
   const int rows_valid = tcount * G;
 
-  const int ps = p.page_size;
+  const int ps = p.page_size, psh = p.page_shift;
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
   const int causal = p.causal;
   const int diag = L - n;
@@ -86,13 +100,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
   const int my_tok = t0 + rl / G;               // token index within the sequence
   const int my_head = g * G + rl % G;
 
+  // A negative scale is applied as a positive one on -q (negating bf16 is
+  // exact), so the running max can be taken on raw scores.
+  const float c = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+
   // ---- Q^T as the B operand of S^T = K . Q^T
   bf16x8 qB[C::DS];
   if (row_ok) {
     const __bf16* qp = (const __bf16*)p.q + (int64_t)(s0 + my_tok) * p.q_stride_tok +
                        (int64_t)my_head * p.q_stride_head + 8 * h2;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) qB[s] = *(const bf16x8*)(qp + 16 * s);
+    for (int s = 0; s < C::DS; ++s) {
+      u32x4 w = *(const u32x4*)(qp + 16 * s);
+      w ^= u32x4{qsign, qsign, qsign, qsign};
+      qB[s] = __builtin_bit_cast(bf16x8, w);
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) qB[s] = bf16x8{};
@@ -109,51 +132,45 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
   const __bf16* vbase = (const __bf16*)p.v_pool + (int64_t)g * p.kv_stride_head;
   PA_LDS char* lds = (PA_LDS char*)smem;
 
-  u32x4 rk[C::LOADS], rv[C::LOADS];
-  auto gload = [&](int blk) {
+  auto gload = [&](int blk, PrefillRegs<D, NW>& r) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * 256 + threadIdx.x;
+      const int idx = i * C::NTH + threadIdx.x;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       const int j = blk * C::KB + kl;
       if (j < L) {
-        const int lp = j / ps;
+        const int lp = j >> psh;
         const int pg = page_of(p, b, lp);
-        const int64_t off = (int64_t)pg * p.kv_stride_page + (int64_t)(j - lp * ps) * p.kv_stride_slot + 8 * cc;
-        rk[i] = *(const u32x4*)(kbase + off);
-        rv[i] = *(const u32x4*)(vbase + off);
+        const int64_t off = (int64_t)pg * p.kv_stride_page + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;
+        r.k[i] = *(const u32x4*)(kbase + off);
+        r.v[i] = *(const u32x4*)(vbase + off);
       } else {
-        rk[i] = u32x4{0u, 0u, 0u, 0u};
-        rv[i] = u32x4{0u, 0u, 0u, 0u};
+        r.k[i] = u32x4{0u, 0u, 0u, 0u};
+        r.v[i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const PrefillRegs<D, NW>& r) {
     PA_LDS char* kl_ = lds + buf * C::STAGE;
     PA_LDS char* vl_ = kl_ + C::KBYTES;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * 256 + threadIdx.x;
+      const int idx = i * C::NTH + threadIdx.x;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
-      *(PA_LDS u32x4*)(kl_ + kl * C::KRS + cc * 16) = rk[i];
-      *(PA_LDS u32x4*)(vl_ + kl * C::VRS + cc * 16) = rv[i];
+      *(PA_LDS u32x4*)(kl_ + kl * C::KRS + cc * 16) = r.k[i];
+      *(PA_LDS u32x4*)(vl_ + kl * C::VRS + cc * 16) = r.v[i];
     }
   };
 
-  if (nblk > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  const int l16 = lane & 15, gq = lane >> 4;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    const bool more = blk + 1 < nblk;
-    if (more) gload(blk + 1);
+  auto compute = [&](int blk) {
     const PA_LDS char* kl_ = lds + (blk & 1) * C::STAGE;
     const PA_LDS char* vl_ = kl_ + C::KBYTES;
     const int kb0 = blk * C::KB;
 
-    // S^T = K . Q^T for two 32-key tiles
+    // S^T = K . Q^T for two 32-key tiles (raw scores)
     f32x16 st[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -169,48 +186,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
       st[kt] = a;
     }
 
-    const bool need_mask = kb0 + C::KB > full_lim;
-    float cmax = kNegInf;
+    if (kb0 + C::KB > full_lim) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = st[kt][r] * p.scale_log2;
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int j = kb0 + 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
           const bool vis = j < L && (!causal || j <= diag + my_tok);
-          v = vis ? v : kNegInf;
+          st[kt][r] = vis ? st[kt][r] : kNegInf;
         }
-        st[kt][r] = v;
-        cmax = fmaxf(cmax, v);
-      }
-    cmax = fmaxf(cmax, shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_safe = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_safe);
-    m_run = m_new;
-
-    u32x4 pk[2][2][2];   // [kt][ks][half]: bf16 P^T operand, 8 values per (kt, ks)
-    float psum = 0.f;
+    }
+    float bmax = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int r = 0; r < 16; r += 2) bmax = fmaxf(bmax, fmaxf(st[kt][r], st[kt][r + 1]));
+    bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+    const float m_blk = bmax * c;               // -inf stays -inf (c > 0)
+    // lazy rescale: move the reference max only when this block exceeds it by > TAU
+    const bool need = m_blk > m_run + C::TAU;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_upd = need ? m_blk : m_run;
+      const float alpha = fast_exp2(m_run - m_upd);   // 1 when unchanged, 0 from -inf
+      l_run *= alpha;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int r0 = 8 * ks + 4 * hh;
-          const uint32_t w0 = pack_bf16x2(fast_exp2(st[kt][r0] - m_safe), fast_exp2(st[kt][r0 + 1] - m_safe));
-          const uint32_t w1 = pack_bf16x2(fast_exp2(st[kt][r0 + 2] - m_safe), fast_exp2(st[kt][r0 + 3] - m_safe));
-          psum += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
-          pk[kt][ks][hh] = u32x4{w0, w1, 0u, 0u};
-        }
-    l_run = alpha * l_run + psum;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+      m_run = m_upd;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
 
-    // O^T += V^T . P^T.  16-lane group q = lane / 16 reads dims
-    // 32*dt + 16*(q & 1) + (lane % 16) of keys kbase + 4*h2 + e and kbase + 8 + 4*h2 + e.
-    const int l16 = lane & 15, gq = lane >> 4;
+    uint32_t pk[2][8];   // bf16 P^T: [kt][ks*4 + word], 8 values per (kt, ks)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float p0 = fast_exp2(fmaf(st[kt][2 * w], c, -m_use));
+        const float p1 = fast_exp2(fmaf(st[kt][2 * w + 1], c, -m_use));
+        pk[kt][w] = pack_bf16x2(p0, p1);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kt][w]), ones, l_run, false);
+      }
+
+    // O^T += V^T . P^T.  16-lane group gq reads dims 32*dt + 16*(gq & 1) + l16
+    // of keys kbase + 4*h2 + e and kbase + 8 + 4*h2 + e.
     const PA_LDS char* vr = vl_ + (4 * h2 + (l16 >> 2)) * C::VRS + 32 * (gq & 1) + 8 * (l16 & 3);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -218,7 +235,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
       for (int ks = 0; ks < 2; ++ks) {
         const int kbase = 32 * kt + 16 * ks;
         const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{pk[kt][ks][0].x, pk[kt][ks][0].y, pk[kt][ks][1].x, pk[kt][ks][1].y});
+            bf16x8, u32x4{pk[kt][4 * ks], pk[kt][4 * ks + 1], pk[kt][4 * ks + 2], pk[kt][4 * ks + 3]});
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const u32x2 a1 = lds_read_tr16(vr + kbase * C::VRS + 64 * dt);
@@ -227,9 +244,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
           acc[dt] = mfma32(va, pb, acc[dt]);
         }
       }
+  };
 
-    if (more) lstore((blk + 1) & 1);
-    __syncthreads();
+  // ---- pipeline: LDS holds block blk (and receives blk+1 after blk is
+  // computed); registers hold blocks blk+1 .. blk+PF, issued PF blocks ahead.
+  PrefillRegs<D, NW> rg[PF];
+  if (nblk > 0) {
+    gload(0, rg[0]);
+    lstore(0, rg[0]);
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (1 + j < nblk) gload(1 + j, rg[j]);
+  }
+  __syncthreads();
+  for (int base = 0; base < nblk; base += PF) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int blk = base + k;
+      if (blk < nblk) {
+        compute(blk);
+        if (blk + 1 < nblk) lstore((blk + 1) & 1, rg[k]);
+        __syncthreads();
+        if (blk + 1 + PF < nblk) gload(blk + 1 + PF, rg[k]);
+      }
+    }
   }
 
   // ---- normalise and write this lane's row (dims 32*dt + 8*(r/4) + 4*h2 + r%4)
@@ -248,10 +286,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
   }
 }
 
+// Tile shape per head size: rows per workgroup (32 per wave) and register
+// prefetch depth, chosen so the kernel fits two waves per SIMD where it can.
+template <int D> struct PrefillShape;
+template <> struct PrefillShape<64> { static constexpr int NW = 8, PF = 2; };
+template <> struct PrefillShape<128> { static constexpr int NW = 8, PF = 2; };
+template <> struct PrefillShape<256> { static constexpr int NW = 4, PF = 1; };
+
+static_assert(32 * PrefillShape<64>::NW == prefill_tile_rows(64), "host and kernel tile rows differ");
+static_assert(32 * PrefillShape<128>::NW == prefill_tile_rows(128), "host and kernel tile rows differ");
+static_assert(32 * PrefillShape<256>::NW == prefill_tile_rows(256), "host and kernel tile rows differ");
+
 template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
+  constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF;
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs;
-  hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)total), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((prefill_kernel<D, NW, PF>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ int main() {
   // mixed batch: prefill + small and large decode tiles
   pa_dims c4 = dims(32, 547, 512, 32, 8, 128, 64, 2000, 128);
   pa::Plan p4 = pa::make_plan(&c4, PA_BF16, 256);
-  CHECK(p4.prefill && p4.tok_per_tile == 32 && p4.num_qtiles == 16 && p4.dec_small && p4.dec_big && p4.big_nt == 4);
+  CHECK(p4.prefill && p4.tok_per_tile == 64 && p4.num_qtiles == 8 && p4.dec_small && p4.dec_big && p4.big_nt == 4);
   CHECK(p4.dec_max_n == 16 && p4.comb_max_n == 16);
   // a 5-token verify bound: 20 rows -> 32-row tile
   pa_dims v5 = dims(4, 20, 5, 32, 8, 128, 64, 100, 16);
