@@ -31,6 +31,11 @@ HIP_FLAGS = [
     "-Rpass-analysis=kernel-resource-usage",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
+# The MFMA kernels take running maxima of scores that are never NaN (keys past
+# the context are zero-filled or masked to -inf): without NaN semantics fmaxf
+# maps to a bare v_max/v_max3 instead of quieting each operand first.
+# Infinities keep their IEEE meaning (the masks rely on -inf).
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
@@ -40,7 +45,7 @@ def _run(cmd):
 
 def _compile_hip(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    rc, out = _run([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj])
+    rc, out = _run([HIPCC, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
     return src, obj, rc, out
 
 

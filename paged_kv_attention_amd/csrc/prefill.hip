@@ -132,21 +132,26 @@ void prefill_kernel(const AttnParams p) {
   const __bf16* vbase = (const __bf16*)p.v_pool + (int64_t)g * p.kv_stride_head;
   PA_LDS char* lds = (PA_LDS char*)smem;
 
+  // The 64 threads of a wave cover 64/CPL consecutive keys of one page, so
+  // the page id is wave-uniform: it comes from a scalar load (counted by
+  // lgkmcnt), and waiting for it never waits for the K/V loads in flight.
   auto gload = [&](int blk, PrefillRegs<D, NW>& r) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NTH + threadIdx.x;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
+      const int jw = __builtin_amdgcn_readfirstlane(blk * C::KB + (i * C::NTH + (threadIdx.x & ~63)) / C::CPL);
       const int j = blk * C::KB + kl;
-      if (j < L) {
-        const int lp = j >> psh;
-        const int pg = page_of(p, b, lp);
-        const int64_t off = (int64_t)pg * p.kv_stride_page + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;
-        r.k[i] = *(const u32x4*)(kbase + off);
-        r.v[i] = *(const u32x4*)(vbase + off);
-      } else {
-        r.k[i] = u32x4{0u, 0u, 0u, 0u};
-        r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      r.k[i] = u32x4{0u, 0u, 0u, 0u};
+      r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (jw < L) {
+        const int lp = jw >> psh;
+        const int64_t pbase = (int64_t)page_of(p, b, lp) * p.kv_stride_page;
+        if (j < L) {
+          const int64_t off = pbase + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;
+          r.k[i] = *(const u32x4*)(kbase + off);
+          r.v[i] = *(const u32x4*)(vbase + off);
+        }
       }
     }
   };
