@@ -46,7 +46,8 @@ struct PrefillCfg {
   static constexpr int CPL = D / 8;              // 16-byte chunks per key row
   static constexpr int LOADS = KB * CPL / NTH;   // 16-byte loads per thread per tensor
   static constexpr int KRS = D * 2 + 16;         // K row stride (bytes)
-  static constexpr int VRS = D * 2 + 32;         // V row stride (bytes)
+  static constexpr int VRS = D * 2 + 64;         // V row stride (bytes): the 4 rows of a transpose
+                                                 // read land 16 banks apart
   static constexpr int KBYTES = KB * KRS;
   static constexpr int STAGE = KBYTES + KB * VRS;
   static constexpr int LDS = 2 * STAGE;
