@@ -36,11 +36,12 @@
 
 namespace pa {
 
-template <int D, int NW, int PF>
+template <int D, int NW, int PF, int KB_ = 64>
 struct PrefillCfg {
   static constexpr int NTH = 64 * NW;            // threads per workgroup
   static constexpr int BM = 32 * NW;             // rows per workgroup
-  static constexpr int KB = 64;                  // keys per block
+  static constexpr int KB = KB_;                 // keys per block
+  static constexpr int KT = KB / 32;             // 32-key MFMA tiles per block
   static constexpr int DS = D / 16;              // k-steps of QK^T
   static constexpr int DT = D / 32;              // 32-dim output tiles
   static constexpr int CPL = D / 8;              // 16-byte chunks per key row
@@ -50,19 +51,20 @@ struct PrefillCfg {
                                                  // read land 16 banks apart
   static constexpr int KBYTES = KB * KRS;
   static constexpr int STAGE = KBYTES + KB * VRS;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int NSTAGE = 2;               // LDS ring depth
+  static constexpr int LDS = NSTAGE * STAGE;
   static constexpr float TAU = 8.f;              // lazy-rescale threshold (log2 units)
 };
 
-template <int D, int NW>
+template <int D, int NW, int KB>
 struct PrefillRegs {
-  u32x4 k[PrefillCfg<D, NW, 1>::LOADS], v[PrefillCfg<D, NW, 1>::LOADS];
+  u32x4 k[PrefillCfg<D, NW, 1, KB>::LOADS], v[PrefillCfg<D, NW, 1, KB>::LOADS];
 };
 
-template <int D, int NW, int PF>
+template <int D, int NW, int PF, int KB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void prefill_kernel(const AttnParams p) {
-  using C = PrefillCfg<D, NW, PF>;
+  using C = PrefillCfg<D, NW, PF, KB>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   // ---- XCD-aware block order: consecutive logical tiles share an XCD
@@ -136,7 +138,7 @@ void prefill_kernel(const AttnParams p) {
   // The 64 threads of a wave cover 64/CPL consecutive keys of one page, so
   // the page id is wave-uniform: it comes from a scalar load (counted by
   // lgkmcnt), and waiting for it never waits for the K/V loads in flight.
-  auto gload = [&](int blk, PrefillRegs<D, NW>& r) {
+  auto gload = [&](int blk, PrefillRegs<D, NW, KB>& r) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NTH + threadIdx.x;
@@ -156,7 +158,7 @@ void prefill_kernel(const AttnParams p) {
       }
     }
   };
-  auto lstore = [&](int buf, const PrefillRegs<D, NW>& r) {
+  auto lstore = [&](int buf, const PrefillRegs<D, NW, KB>& r) {
     PA_LDS char* kl_ = lds + buf * C::STAGE;
     PA_LDS char* vl_ = kl_ + C::KBYTES;
 #pragma unroll
@@ -171,15 +173,11 @@ void prefill_kernel(const AttnParams p) {
   const int l16 = lane & 15, gq = lane >> 4;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute = [&](int blk) {
-    const PA_LDS char* kl_ = lds + (blk & 1) * C::STAGE;
-    const PA_LDS char* vl_ = kl_ + C::KBYTES;
-    const int kb0 = blk * C::KB;
-
-    // S^T = K . Q^T for two 32-key tiles (raw scores)
-    f32x16 st[2];
+  // S^T = K . Q^T for the 32-key tiles of block blk (raw scores)
+  auto qk = [&](int blk, f32x16 (&st)[C::KT]) {
+    const PA_LDS char* kl_ = lds + (blk % C::NSTAGE) * C::STAGE;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < C::KT; ++kt) {
       f32x16 a;
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = 0.f;
@@ -191,10 +189,14 @@ void prefill_kernel(const AttnParams p) {
       }
       st[kt] = a;
     }
+  };
 
+  // Mask, online-softmax update and bf16 P^T of block blk.
+  auto softmax = [&](int blk, f32x16 (&st)[C::KT], uint32_t (&pk)[C::KT][8]) {
+    const int kb0 = blk * C::KB;
     if (kb0 + C::KB > full_lim) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb0 + 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
@@ -204,7 +206,7 @@ void prefill_kernel(const AttnParams p) {
     }
     float bmax = kNegInf;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) bmax = fmaxf(bmax, fmaxf(st[kt][r], st[kt][r + 1]));
     bmax = fmaxf(bmax, shfl_xor(bmax, 32));
@@ -220,10 +222,8 @@ void prefill_kernel(const AttnParams p) {
       m_run = m_upd;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
-
-    uint32_t pk[2][8];   // bf16 P^T: [kt][ks*4 + word], 8 values per (kt, ks)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const float p0 = fast_exp2(fmaf(st[kt][2 * w], c, -m_use));
@@ -231,12 +231,15 @@ void prefill_kernel(const AttnParams p) {
         pk[kt][w] = pack_bf16x2(p0, p1);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kt][w]), ones, l_run, false);
       }
+  };
 
-    // O^T += V^T . P^T.  16-lane group gq reads dims 32*dt + 16*(gq & 1) + l16
-    // of keys kbase + 4*h2 + e and kbase + 8 + 4*h2 + e.
+  // O^T += V^T . P^T for block blk.  16-lane group gq reads dims
+  // 32*dt + 16*(gq & 1) + l16 of keys kbase + 4*h2 + e and kbase + 8 + 4*h2 + e.
+  auto pv = [&](int blk, const uint32_t (&pk)[C::KT][8]) {
+    const PA_LDS char* vl_ = lds + (blk % C::NSTAGE) * C::STAGE + C::KBYTES;
     const PA_LDS char* vr = vl_ + (4 * h2 + (l16 >> 2)) * C::VRS + 32 * (gq & 1) + 8 * (l16 & 3);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int kbase = 32 * kt + 16 * ks;
@@ -252,9 +255,11 @@ void prefill_kernel(const AttnParams p) {
       }
   };
 
-  // ---- pipeline: LDS holds block blk (and receives blk+1 after blk is
-  // computed); registers hold blocks blk+1 .. blk+PF, issued PF blocks ahead.
-  PrefillRegs<D, NW> rg[PF];
+  // ---- LDS holds block blk (and receives blk+1 after blk is computed);
+  // registers hold blocks blk+1 .. blk+PF, issued PF blocks ahead.
+  f32x16 st[C::KT];
+  uint32_t pk[C::KT][8];
+  PrefillRegs<D, NW, KB> rg[PF];
   if (nblk > 0) {
     gload(0, rg[0]);
     lstore(0, rg[0]);
@@ -268,7 +273,9 @@ void prefill_kernel(const AttnParams p) {
     for (int k = 0; k < PF; ++k) {
       const int blk = base + k;
       if (blk < nblk) {
-        compute(blk);
+        qk(blk, st);
+        softmax(blk, st, pk);
+        pv(blk, pk);
         if (blk + 1 < nblk) lstore((blk + 1) & 1, rg[k]);
         __syncthreads();
         if (blk + 1 + PF < nblk) gload(blk + 1 + PF, rg[k]);
@@ -295,9 +302,9 @@ void prefill_kernel(const AttnParams p) {
 // Tile shape per head size: rows per workgroup (32 per wave) and register
 // prefetch depth, chosen so the kernel fits two waves per SIMD where it can.
 template <int D> struct PrefillShape;
-template <> struct PrefillShape<64> { static constexpr int NW = 8, PF = 2; };
-template <> struct PrefillShape<128> { static constexpr int NW = 8, PF = 2; };
-template <> struct PrefillShape<256> { static constexpr int NW = 4, PF = 1; };
+template <> struct PrefillShape<64> { static constexpr int NW = 8, PF = 2, KB = 64; };
+template <> struct PrefillShape<128> { static constexpr int NW = 8, PF = 2, KB = 64; };
+template <> struct PrefillShape<256> { static constexpr int NW = 4, PF = 1, KB = 64; };
 
 static_assert(32 * PrefillShape<64>::NW == prefill_tile_rows(64), "host and kernel tile rows differ");
 static_assert(32 * PrefillShape<128>::NW == prefill_tile_rows(128), "host and kernel tile rows differ");
@@ -305,9 +312,9 @@ static_assert(32 * PrefillShape<256>::NW == prefill_tile_rows(256), "host and ke
 
 template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
-  constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF;
+  constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF, KB = PrefillShape<D>::KB;
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs;
-  hipLaunchKernelGGL((prefill_kernel<D, NW, PF>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
