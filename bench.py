@@ -173,6 +173,113 @@ class PrefillBench:
                                        out=self.out, max_query_len=self.mql)
 
 
+class WorkloadBench:
+    """Any seeded workload on device, pools rotated over `layers` sets."""
+
+    def __init__(self, config, layers=1):
+        import torch
+        import paged_kv_attention_amd as pa
+        from workloads import make
+        self.torch, self.pa = torch, pa
+        self.w = w = make(config)
+        dev = torch.device("cuda", 0)
+        self.q = w.q.to(dev)
+        self.bt = w.block_tables.to(dev)
+        self.cl = w.context_lens.to(dev)
+        self.qsl = w.query_start_loc.to(dev)
+        self.pools = [(pa.pool_like(w.k_pool, dev), pa.pool_like(w.v_pool, dev))]
+        gen = torch.Generator(device=dev).manual_seed(4321)
+        P, ps, Hkv, D = w.k_pool.shape
+        for _ in range(layers - 1):
+            k = pa.empty_pool(P, ps, Hkv, D, dtype=w.dtype, device=dev)
+            v = pa.empty_pool(P, ps, Hkv, D, dtype=w.dtype, device=dev)
+            k.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
+            v.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
+            self.pools.append((k, v))
+        self.out = torch.empty_like(self.q)
+        dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=w.max_query_len)
+        self.ws = torch.empty(max(pa.workspace_size(dims, w.dtype), 16), dtype=torch.uint8, device=dev)
+        self.splits = pa.choose_splits(dims)
+        lens = w.context_lens.tolist()
+        e = 4 if w.dtype == torch.float32 else 2
+        self.bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, ps, e)
+        self.flops = algorithmic_flops(lens, w.query_lens, w.num_q_heads, w.head_dim)
+
+    def attend(self, layer):
+        k, v = self.pools[layer % len(self.pools)]
+        w = self.w
+        return self.pa.paged_attention(self.q, k, v, self.bt, self.cl, self.qsl, w.scale, w.causal, out=self.out,
+                                       workspace=self.ws, max_query_len=w.max_query_len)
+
+    def parity(self, tokens):
+        from oracle import attention_f64
+        torch = self.torch
+        out = self.attend(0).cpu()
+        w = self.w
+        ref = attention_f64(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
+                            tokens=tokens)
+        idx = torch.tensor(tokens)
+        return torch.max(torch.abs(out.index_select(0, idx).double() - ref.index_select(0, idx))).item()
+
+
+def other_workloads(steps, warmup):
+    """Latency of the fp32 single-sequence decode, GB/s of the ragged decode
+    batch and of the mixed batch (their HBM-bound rooflines), with pools
+    rotated so the Infinity Cache cannot hold them."""
+    import torch
+    res = {}
+    for cfg, layers, name in [(1, 1, "fp32 single-sequence decode, 8/2 heads, D 64, page 16, ctx 600"),
+                              (2, 8, "bf16 ragged decode, 32 seqs, ctx U{1..4096}, 32/8 heads, D 128, page 64"),
+                              (4, 8, "bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify")]:
+        print(f"[bench] other workload {cfg}: building inputs", file=sys.stderr, flush=True)
+        wb = WorkloadBench(cfg, layers)
+        qsl = wb.w.query_start_loc.tolist()
+        toks = sorted(set([0, qsl[-1] - 1] + [qsl[b] for b in range(0, wb.w.num_seqs, 7)]))
+        err = wb.parity(toks)
+        _, per = _time_steps([wb.attend], steps, warmup)
+        ms = per[0]
+        entry = {"workload": name, "ms": round(ms, 5), "splits": wb.splits, "parity_max_abs_err": err,
+                 "algorithmic_bytes": wb.bytes, "GB_s": round(wb.bytes / (ms * 1e-3) / 1e9, 2),
+                 "hbm_frac": round(wb.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "algorithmic_flops": wb.flops, "pool_sets_rotated": layers}
+        res[f"config{cfg}"] = entry
+        del wb
+        torch.cuda.empty_cache()
+    return res
+
+
+def graph_step(db, steps):
+    """The decode step (write + attention) captured once in a hipGraph and
+    replayed over the rotated pool sets: launch overhead removed."""
+    import torch
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for layer in range(len(db.pools)):       # warm the launch path on this stream
+            db.write(layer)
+            db.attend(layer)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for layer in range(len(db.pools)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            db.write(layer)
+            db.attend(layer)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def _time_steps(step_fns, steps, warmup):
     """Run warmup, then time `steps` steps; each fn in step_fns is timed with
     HIP events on the current stream.  Returns (total_ms, [avg ms per fn])."""
@@ -235,6 +342,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the other measured workloads")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay of the decode step")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -296,6 +405,11 @@ def main():
             "kv_write_ms": round(per[0], 5),
             "parity_max_abs_err": err,
         })
+        if not args.no_graph:
+            g_ms = graph_step(db, args.steps)
+            result["graph_step"] = {"ms_per_step": round(g_ms, 5),
+                                    "GB_s": round(db.attn_bytes / (g_ms * 1e-3) / 1e9, 2),
+                                    "note": "kv_cache_write + paged_attention captured in one hipGraph per pool set"}
         decode_w = db.w
         del db
         torch.cuda.empty_cache()
@@ -326,6 +440,9 @@ def main():
             result["prefill"] = pre
         del pb
         torch.cuda.empty_cache()
+
+    if args.only is None and not args.no_others:
+        result["other_workloads"] = other_workloads(args.steps, args.warmup)
 
     if not args.no_cpu_baseline and args.only is None and decode_w is not None:
         print("[bench] cpu baseline: timing the float64 oracle", file=sys.stderr, flush=True)

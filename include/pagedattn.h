@@ -126,25 +126,31 @@ pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, voi
 
 /*
  * pa_workspace_size -- bytes of workspace paged_attention needs for these
- * dims: num_splits * (rows) * (D + 2) * 4 when split-KV partials are used
- * (float32 accumulator, running max and sum per split; page "Attention
- * kernels", Decode: GQA packing and split-KV), else 0.  Returns 0 for
- * invalid dims as well; paged_attention reports those.
+ * dims: S * B * T * Hq * (D + 2) * 4 when split-KV partials are used, else 0.
+ * S is the largest split count of the call's launches, T the query tokens per
+ * sequence the split launches can take (min(max_query_len, 16, 64/G) for
+ * bf16, max_query_len for float32).  Each partial is a float32 accumulator
+ * with its running max and sum (page "Attention kernels", Decode: GQA packing
+ * and split-KV).  Prefill tokens take no workspace.  Returns 0 for invalid
+ * dims as well; paged_attention reports those.
  */
 size_t pa_workspace_size(const pa_dims* dims, pa_dtype dtype);
 
 /*
- * pa_choose_splits -- the split count paged_attention will use for these
- * dims: dims->num_splits when > 0, else enough workgroups to fill every CU of
- * the current device with a minimum number of pages per split (page "32.
- * Production attention kernels", How many splits?).  Returns 1 for invalid dims.
+ * pa_choose_splits -- the split count paged_attention will use for decode
+ * rows (one token, or n*G <= 16 rows): dims->num_splits when > 0, else enough
+ * workgroups to fill every CU of the current device with at least 256 keys
+ * per split and at most 32 splits (page "32. Production attention kernels",
+ * How many splits?).  Verification blocks (16 < n*G <= 64 rows) use 8 splits
+ * unless dims->num_splits is set.  Returns 1 for invalid dims.
  */
 int32_t pa_choose_splits(const pa_dims* dims);
 
 /*
  * pa_validate -- SYNCHRONOUS debug/test check of device metadata.
  * Copies the metadata to the host and checks: 0 <= qsl[b] <= qsl[b+1],
- * qsl[0] == 0, qsl[B] == N; 0 <= context_lens[b] <= W*ps; n <= L when
+ * qsl[0] == 0, qsl[B] == N; n <= max_query_len when that bound is set;
+ * 0 <= context_lens[b] <= W*ps; n <= L when
  * causal (a token with pos < 0 sees nothing); every block-table entry a
  * sequence uses lies in [0, P); and, when slot_mapping is not NULL, every
  * slot is -1 or in [0, P*ps) and no slot repeats (page "Attention and KV

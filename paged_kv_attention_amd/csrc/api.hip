@@ -87,9 +87,10 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
   p.context_lens = context_lens;
   p.query_start_loc = query_start_loc;
   const int N = dims->num_tokens, Hq = dims->num_q_heads;
-  if (pl.splits > 1) {
+  const int smax = pl.splits > pl.splits_big ? pl.splits : pl.splits_big;
+  if (smax > 1) {
     p.ws_acc = (float*)workspace;
-    p.ws_ml = (float*)workspace + (size_t)pl.splits * N * Hq * dims->head_dim;
+    p.ws_ml = (float*)workspace + (size_t)smax * dims->num_seqs * pl.ws_tok * Hq * dims->head_dim;
   }
   p.q_stride_tok = dims->q_stride_tok;
   p.q_stride_head = dims->q_stride_head;
@@ -117,6 +118,9 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
   p.num_qtiles = pl.num_qtiles;
   p.comb_max_n = pl.comb_max_n;
   p.comb_tokens = pl.comb_tokens;
+  p.ws_tok = pl.ws_tok;
+  p.comb_splits_small = pl.dec_small || dtype == PA_F32 ? pl.splits : 1;
+  p.comb_splits_big = pl.dec_big || dtype == PA_F32 ? pl.splits_big : 1;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
@@ -135,6 +139,8 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
       AttnParams q2 = p;
       q2.row_lo = 16;
       q2.row_hi = 16 * pl.big_nt;
+      q2.num_splits = pl.splits_big;
+      q2.pages_per_split = pl.pages_per_split_big;
       e = launch_decode(q2, pl.big_nt, s);
     }
     if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);

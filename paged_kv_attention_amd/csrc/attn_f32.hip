@@ -89,14 +89,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     }
   }
 
-  const int64_t NH = (int64_t)p.num_tokens * p.num_q_heads;
+  const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
   if (S == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* op = (float*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) op[lane + 64 * i] = acc[i] * inv;
   } else {
-    const int64_t ri = (int64_t)split * NH + (int64_t)tok * p.num_q_heads + h;
+    const int64_t ri = (int64_t)split * NH + ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) p.ws_acc[ri * D + lane + 64 * i] = acc[i];
     if (lane == 0) {
@@ -139,10 +139,13 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnParams p) {
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
   if (t >= n || n > p.comb_max_n) return;
+  // rows of the 16-row decode tile and of the verify tile may use different
+  // split counts; a class with one split was written by its decode kernel
+  const int S = n * p.group <= 16 ? p.comb_splits_small : p.comb_splits_big;
+  if (S <= 1) return;
   const int tok = s0 + t;
-  const int64_t NH = (int64_t)p.num_tokens * p.num_q_heads;
-  const int64_t row = (int64_t)tok * p.num_q_heads + h;
-  const int S = p.num_splits;
+  const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
+  const int64_t row = ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
   float M = kNegInf;
   for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(s * NH + row) * 2]);
   const float Ms = M == kNegInf ? 0.f : M;

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   }
 
   const int nrows = min(rows, ROWS);
-  const int NH = p.num_tokens * p.num_q_heads;
+  const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
   for (int it = threadIdx.x; it < nrows * (D / 4); it += 256) {
     const int row = it / (D / 4), c4 = it % (D / 4);
     const int tok = s0 + row / G, head = g * G + row % G;
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
       *(u32x2*)op = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
     } else {
-      const int64_t ri = (int64_t)split * NH + (int64_t)tok * p.num_q_heads + head;
+      const int64_t ri = (int64_t)split * NH + ((int64_t)b * p.ws_tok + row / G) * p.num_q_heads + head;
       *(f32x4*)(p.ws_acc + ri * D + 4 * c4) = o;
       if (c4 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{M, Lt};
     }

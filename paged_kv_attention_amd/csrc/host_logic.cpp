@@ -52,8 +52,10 @@ int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count) {
   if (cu_count < 1) cu_count = 1;
   // units of parallel work per split: (sequence, KV head) workgroups of 4 waves
   // for the bf16 decode kernel, (token, query head) waves for float32.
+  const int N = d->num_tokens;
+  const int mql = d->max_query_len > 0 && d->max_query_len < N ? d->max_query_len : N;
   int64_t units = dtype == PA_BF16 ? (int64_t)d->num_seqs * d->num_kv_heads
-                                   : (int64_t)d->num_seqs * d->num_q_heads;
+                                   : (int64_t)d->num_seqs * d->num_q_heads * (mql > 0 ? mql : 1);
   int64_t target = dtype == PA_BF16 ? 2 * (int64_t)cu_count : 8 * (int64_t)cu_count;
   if (units < 1) units = 1;
   int64_t want = (target + units - 1) / units;
@@ -85,17 +87,39 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count) {
     pl.prefill = pl.mql > pl.dec_max_n;
     pl.tok_per_tile = prefill_tile_rows(d->head_dim) / G;
     pl.num_qtiles = pl.prefill ? (pl.mql + pl.tok_per_tile - 1) / pl.tok_per_tile : 0;
-    pl.combine = pl.splits > 1 && dmax >= 1;
+    // The verify-tile launch (n*G > 16) serves few sequences, so its pages
+    // are cut into 8 splits of >= 256 keys (page "Attention kernels", Decode:
+    // verify steps use 8 splits).
+    if (d->num_splits > 0) {
+      pl.splits_big = pl.splits;
+      pl.pages_per_split_big = pl.pages_per_split;
+    } else {
+      const int min_pages = (256 + d->page_size - 1) / d->page_size;
+      int ppb = (W + 7) / 8;
+      if (ppb < min_pages) ppb = min_pages;
+      pl.pages_per_split_big = ppb;
+      pl.splits_big = (W + ppb - 1) / ppb;
+    }
+    if (!pl.dec_big) pl.splits_big = 1;
+    pl.combine = dmax >= 1 && ((pl.dec_small && pl.splits > 1) || (pl.dec_big && pl.splits_big > 1));
     pl.comb_tokens = dmax;
     pl.comb_max_n = pl.dec_max_n;
+    pl.ws_tok = dmax;
   } else {
     pl.dec_max_n = 0;
+    pl.splits_big = pl.splits;
+    pl.pages_per_split_big = pl.pages_per_split;
     pl.combine = pl.splits > 1 && pl.mql >= 1;
     pl.comb_tokens = pl.mql;
     pl.comb_max_n = INT_MAX;
+    pl.ws_tok = pl.mql;
   }
-  if (pl.splits > 1)
-    pl.workspace_bytes = (size_t)pl.splits * (size_t)N * (size_t)d->num_q_heads * ((size_t)d->head_dim + 2) * 4;
+  const int smax = pl.splits > pl.splits_big ? pl.splits : pl.splits_big;
+  // split partials are indexed by (sequence, token of the step) over the
+  // split classes only, so prefill tokens take no workspace
+  if (smax > 1)
+    pl.workspace_bytes = (size_t)smax * (size_t)d->num_seqs * (size_t)pl.ws_tok * (size_t)d->num_q_heads *
+                         ((size_t)d->head_dim + 2) * 4;
   return pl;
 }
 
@@ -106,6 +130,7 @@ pa_status validate_host(const int32_t* bt, const int32_t* lens, const int32_t* q
   for (int b = 0; b < B; ++b) {
     const int n = qsl[b + 1] - qsl[b];
     if (n < 0) return PA_ERR_INVALID_DATA;
+    if (d->max_query_len > 0 && n > d->max_query_len) return PA_ERR_INVALID_DATA;
     const int L = lens[b];
     if (L < 0 || (int64_t)L > (int64_t)W * ps) return PA_ERR_INVALID_DATA;
     if (causal && n > L) return PA_ERR_INVALID_DATA;

@@ -12,8 +12,10 @@ namespace pa {
 
 struct Plan {
   int mql;                 // effective max_query_len
-  int splits;              // S after sizing (>= 1)
+  int splits;              // S after sizing (>= 1); bf16: the 16-row decode tile's launch
   int pages_per_split;     // ceil(W / S)
+  int splits_big;          // bf16: splits of the 32/64-row (verify) tile's launch
+  int pages_per_split_big;
   int dec_max_n;           // bf16: sequences with n <= dec_max_n use the decode kernel
   bool dec_small;          // bf16: decode launch for n*G <= 16 (16-row tile)
   bool dec_big;            // bf16: decode launch for 16 < n*G <= 16*big_nt
@@ -24,6 +26,7 @@ struct Plan {
   bool combine;            // split partials need the combine launch
   int comb_tokens;         // combine: token slots per sequence
   int comb_max_n;          // combine: sequences with n <= comb_max_n
+  int ws_tok;              // workspace row slots per sequence
   size_t workspace_bytes;  // bytes the call needs
 };
 

@@ -20,8 +20,9 @@ struct AttnParams {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start_loc;
-  float* ws_acc;            // [S][N*Hq][D] float32 split accumulators
-  float* ws_ml;             // [S][N*Hq][2] float32 (running max in log2 units, sum)
+  float* ws_acc;            // [S][B*ws_tok*Hq][D] float32 split accumulators
+  float* ws_ml;             // [S][B*ws_tok*Hq][2] float32 (running max in log2 units, sum)
+  int32_t ws_tok;           // workspace row slots per sequence (tokens of the split classes)
   int64_t q_stride_tok, q_stride_head;
   int64_t o_stride_tok, o_stride_head;
   int64_t kv_stride_page, kv_stride_slot, kv_stride_head;
@@ -37,6 +38,8 @@ struct AttnParams {
   int32_t num_qtiles;       // prefill: tiles per (sequence, KV head)
   int32_t comb_max_n;       // combine: sequences with n <= comb_max_n
   int32_t comb_tokens;      // combine: token slots per sequence in the grid
+  int32_t comb_splits_small;  // combine: splits of rows with n*G <= 16 (1 = written by the decode kernel)
+  int32_t comb_splits_big;    // combine: splits of rows with n*G > 16
 };
 
 struct KvWriteParams {

@@ -34,6 +34,14 @@ int main() {
   pa::Plan p4 = pa::make_plan(&c4, PA_BF16, 256);
   CHECK(p4.prefill && p4.tok_per_tile == 64 && p4.num_qtiles == 8 && p4.dec_small && p4.dec_big && p4.big_nt == 4);
   CHECK(p4.dec_max_n == 16 && p4.comb_max_n == 16);
+  // the verify-tile launch uses 8 splits of 16 pages; partials only for the 16 decode-class token slots
+  CHECK(p4.splits == 2 && p4.splits_big == 8 && p4.pages_per_split_big == 16 && p4.ws_tok == 16);
+  CHECK(p4.workspace_bytes == (size_t)8 * 32 * 16 * 32 * 130 * 4);
+  // long prefill: no decode rows can split, so prefill tokens take no workspace beyond 16 slots
+  pa_dims c5 = dims(4, 32768, 8192, 32, 8, 128, 64, 512, 128);
+  pa::Plan p5 = pa::make_plan(&c5, PA_BF16, 256);
+  CHECK(p5.prefill && p5.num_qtiles == 128 && p5.ws_tok == 16);
+  CHECK(p5.workspace_bytes == (size_t)p5.splits * 4 * 16 * 32 * 130 * 4 && p5.splits >= p5.splits_big);
   // a 5-token verify bound: 20 rows -> 32-row tile
   pa_dims v5 = dims(4, 20, 5, 32, 8, 128, 64, 100, 16);
   pa::Plan pv = pa::make_plan(&v5, PA_BF16, 256);
@@ -77,6 +85,9 @@ int main() {
   qsl = {0, 2, 3}; lens[1] = 0;   // one token over an empty context under causal
   CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 1, &v) == PA_ERR_INVALID_DATA);
   CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 0, &v) == PA_OK);
+  v.max_query_len = 1;      // sequence 0 has 2 tokens
+  CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), nullptr, 0, 0, &v) == PA_ERR_INVALID_DATA);
+  v.max_query_len = 0;
   lens[1] = 5; slots = {5, 5, -1};
   CHECK(pa::validate_host(bt.data(), lens.data(), qsl.data(), slots.data(), 3, 1, &v) == PA_ERR_INVALID_DATA);
   slots = {64, -1, 0};
