@@ -35,8 +35,12 @@ if ROOT not in sys.path:
 METRIC = "decode attention HBM GB/s (% of peak) at 64×4096 ctx; prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
-DECODE_KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_amd", "csrc", "decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_traffic.json")
+CSRC = os.path.join(ROOT, "paged_kv_attention_amd", "csrc")
+# Measured HBM traffic per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
+# a plain copy's counts) is kept next to the hash of the sources it was taken
+# from; a kernel changed since then reports traffic null.
+TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.json"), "decode.hip"),
+                 "prefill": (os.path.join(ROOT, "profiles", "prefill_c5_traffic.json"), "prefill.hip")}
 
 
 # ----------------------------------------------------------------------------- accounting
@@ -67,9 +71,22 @@ def kv_write_bytes(tokens, num_kv_heads, head_dim, elem_bytes):
     return 2 * 2 * tokens * num_kv_heads * head_dim * elem_bytes + 4 * tokens
 
 
-def _src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_src_hash(kernel_file):
+    """Hash of a kernel's source and the device headers it includes."""
+    h = hashlib.sha256()
+    for name in (kernel_file, "pa_device.h", "pa_params.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(which):
+    path, src = TRAFFIC_FILES[which]
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    return tr.get("bytes_per_launch") if tr.get("src_sha256_16") == kernel_src_hash(src) else None
 
 
 # ----------------------------------------------------------------------------- GPU workloads
@@ -382,12 +399,7 @@ def main():
         value = db.attn_bytes / (ms * 1e-3) / 1e9
         kern_ms = per[1]
         achieved = db.attn_bytes / (kern_ms * 1e-3) / 1e9
-        traffic = None
-        if os.path.exists(TRAFFIC_FILE):
-            with open(TRAFFIC_FILE) as f:
-                tr = json.load(f)
-            if tr.get("decode_src_sha256_16") == _src_hash(DECODE_KERNEL_SRC):
-                traffic = tr.get("bytes_per_launch")
+        traffic = measured_traffic("decode")
         result.update({
             "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -429,7 +441,8 @@ def main():
                "algorithmic_flops": pb.flops,
                "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops_kernel / BF16_PEAK_TFLOPS, 4),
-                            "traffic": None, "kernel": "prefill_kernel<128>", "kernel_ms": round(kern_ms, 4)}}
+                            "traffic": measured_traffic("prefill"), "kernel": "prefill_kernel<128>",
+                            "kernel_ms": round(kern_ms, 4)}}
         if args.only == "prefill":
             result.update({"metric": METRIC, "value": round(tflops_kernel, 2), "unit": "TFLOP/s", "n_gpus": 1,
                            "steps": psteps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),

@@ -11,11 +11,20 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All buffers are device memory owned by the caller.  The library
- *   allocates nothing per call, keeps no per-call state and never reads
- *   device memory back in paged_attention / kv_cache_write, so both can be
- *   captured in a hipGraph; the only cached state is the CU count per device.
+ *   allocates no memory, keeps no per-call state and never reads device
+ *   memory back in paged_attention / kv_cache_write, so both can be captured
+ *   in a hipGraph.  Cached per device: the CU count, and two side streams
+ *   with three events (default priority), created by the first bf16 call
+ *   outside graph capture that launches more than one tile class (16-row
+ *   decode tiles, verification tiles, prefill tiles: decided on the host from
+ *   max_query_len and the group size) and kept until the process ends.  A
+ *   graph captured before they exist gets serial launches.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
- *   void*; NULL = the default stream).  Nothing is synchronised.
+ *   void*; NULL = the default stream).  Nothing is synchronised.  A mixed
+ *   call forks into the side streams through an event recorded on `stream`
+ *   and joins them back into `stream` before returning, so all of its work is
+ *   ordered before anything enqueued on `stream` afterwards.  Calls from
+ *   several host threads are serialised while they enqueue.
  * - Element types: PA_F32 or PA_BF16 for q, out, pools and new rows.  All
  *   metadata is int32.
  * - Strides are in elements.  The head dimension must be contiguous.

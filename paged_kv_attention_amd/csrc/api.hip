@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "host_logic.h"
@@ -31,6 +32,54 @@ static int cu_count() {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Two side streams and their events per device, so the launches of a mixed
+// batch (prefill tiles, 16-row decode tiles, verification tiles) run side by
+// side instead of one after another: a prefill launch alone fills few CUs
+// (page "Attention kernels", Open questions: a chunk's tiles versus the
+// chip's CUs).  They are created once, on the first mixed call made outside
+// graph capture, at the default priority, and live until the process ends.
+// The caller's stream forks into them through an event and joins them again
+// before paged_attention returns, so the call stays stream-ordered and
+// capturable.
+struct SideStreams {
+  std::mutex mu;
+  bool ready = false, failed = false;
+  hipStream_t side[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr, join[2] = {nullptr, nullptr};
+};
+static SideStreams g_side[64];
+
+// Returns the device's side streams with their mutex held, or nullptr.
+static SideStreams* lock_side_streams(hipStream_t caller) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStreams& ss = g_side[dev];
+  ss.mu.lock();
+  if (!ss.ready && !ss.failed) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      ss.mu.unlock();
+      return nullptr;                      // nothing is created while a graph is being captured
+    }
+    bool ok = hipStreamCreateWithFlags(&ss.side[0], hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&ss.side[1], hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&ss.join[0], hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&ss.join[1], hipEventDisableTiming) == hipSuccess;
+    if (ok) {
+      ss.ready = true;
+    } else {
+      ss.failed = true;                    // serial launches from now on
+      (void)hipGetLastError();
+    }
+  }
+  if (!ss.ready) {
+    ss.mu.unlock();
+    return nullptr;
+  }
+  return &ss;
+}
 
 }  // namespace pa
 
@@ -128,21 +177,45 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
     e = launch_f32(p, pl.mql, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, false, s);
   } else {
+    AttnParams q1 = p;                       // 16-row decode tiles
+    q1.row_lo = 0;
+    q1.row_hi = 16;
+    AttnParams q2 = p;                       // verification tiles
+    q2.row_lo = 16;
+    q2.row_hi = 16 * pl.big_nt;
+    q2.num_splits = pl.splits_big;
+    q2.pages_per_split = pl.pages_per_split_big;
+    const int classes = (int)pl.prefill + (int)pl.dec_small + (int)pl.dec_big;
+    SideStreams* ss = classes >= 2 ? lock_side_streams(s) : nullptr;
+    if (ss) {
+      // prefill on side 0, verification on side 1 (when 16-row tiles are
+      // launched too), 16-row tiles and the combine on the caller's stream;
+      // the combine waits for side 1, the return for side 0
+      const bool p_side = pl.prefill, v_side = pl.dec_big && pl.dec_small;
+      e = hipEventRecord(ss->fork, s);
+      bool p_fork = false, v_fork = false;   // side streams that joined this call
+      if (e == hipSuccess && p_side) p_fork = (e = hipStreamWaitEvent(ss->side[0], ss->fork, 0)) == hipSuccess;
+      if (e == hipSuccess && v_side) v_fork = (e = hipStreamWaitEvent(ss->side[1], ss->fork, 0)) == hipSuccess;
+      if (e == hipSuccess && p_side) e = launch_prefill(p, ss->side[0]);
+      if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, v_side ? ss->side[1] : s);
+      if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
+      if (v_fork) {                          // joined even after a failed launch
+        hipError_t j = hipEventRecord(ss->join[1], ss->side[1]);
+        if (j == hipSuccess) j = hipStreamWaitEvent(s, ss->join[1], 0);
+        if (e == hipSuccess) e = j;
+      }
+      if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
+      if (p_fork) {
+        hipError_t j = hipEventRecord(ss->join[0], ss->side[0]);
+        if (j == hipSuccess) j = hipStreamWaitEvent(s, ss->join[0], 0);
+        if (e == hipSuccess) e = j;
+      }
+      ss->mu.unlock();
+      return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
     if (pl.prefill) e = launch_prefill(p, s);
-    if (e == hipSuccess && pl.dec_small) {
-      AttnParams q1 = p;
-      q1.row_lo = 0;
-      q1.row_hi = 16;
-      e = launch_decode(q1, 1, s);
-    }
-    if (e == hipSuccess && pl.dec_big) {
-      AttnParams q2 = p;
-      q2.row_lo = 16;
-      q2.row_hi = 16 * pl.big_nt;
-      q2.num_splits = pl.splits_big;
-      q2.pages_per_split = pl.pages_per_split_big;
-      e = launch_decode(q2, pl.big_nt, s);
-    }
+    if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
+    if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

@@ -64,6 +64,18 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
+// Reductions across the two 32-lane halves of a wave (lane i with lane i^32)
+// on the gfx950 half swap, which stays in the VALU (no LDS round trip).  The
+// swap returns, in some order, the lane's own value and its partner's.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
   return v;

@@ -176,18 +176,39 @@ void prefill_kernel(const AttnParams p) {
   // S^T = K . Q^T for the 32-key tiles of block blk (raw scores)
   auto qk = [&](int blk, f32x16 (&st)[C::KT]) {
     const PA_LDS char* kl_ = lds + (blk % C::NSTAGE) * C::STAGE;
+    if constexpr (C::KT * C::DS <= 16) {
+      // every K fragment of the block is requested before the first MFMA, so
+      // the LDS latency is paid once per block rather than once per pair
+      bf16x8 ka[C::KT][C::DS];
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
-      f32x16 a;
+      for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] = 0.f;
-      const PA_LDS char* kr = kl_ + (32 * kt + l32) * C::KRS + 16 * h2;
+        for (int s = 0; s < C::DS; ++s)
+          ka[kt][s] = *(const PA_LDS bf16x8*)(kl_ + (32 * kt + l32) * C::KRS + 16 * h2 + 32 * s);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
-        const bf16x8 ka = *(const PA_LDS bf16x8*)(kr + 32 * s);
-        a = mfma32(ka, qB[s], a);
+      for (int kt = 0; kt < C::KT; ++kt) {
+        f32x16 a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) a = mfma32(ka[kt][s], qB[s], a);
+        st[kt] = a;
       }
-      st[kt] = a;
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt) {
+        f32x16 a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = 0.f;
+        const PA_LDS char* kr = kl_ + (32 * kt + l32) * C::KRS + 16 * h2;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          const bf16x8 ka = *(const PA_LDS bf16x8*)(kr + 32 * s);
+          a = mfma32(ka, qB[s], a);
+        }
+        st[kt] = a;
+      }
     }
   };
 
@@ -209,7 +230,7 @@ void prefill_kernel(const AttnParams p) {
     for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) bmax = fmaxf(bmax, fmaxf(st[kt][r], st[kt][r + 1]));
-    bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+    bmax = xor32_max(bmax);
     const float m_blk = bmax * c;               // -inf stays -inf (c > 0)
     // lazy rescale: move the reference max only when this block exceeds it by > TAU
     const bool need = m_blk > m_run + C::TAU;
@@ -284,7 +305,7 @@ void prefill_kernel(const AttnParams p) {
   }
 
   // ---- normalise and write this lane's row (dims 32*dt + 8*(r/4) + 4*h2 + r%4)
-  l_run += shfl_xor(l_run, 32);
+  l_run = xor32_sum(l_run);
   if (row_ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     __bf16* op = (__bf16*)p.out + (int64_t)(s0 + my_tok) * p.o_stride_tok + (int64_t)my_head * p.o_stride_head + 4 * h2;
