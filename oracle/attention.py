@@ -32,6 +32,21 @@ Readings where the pages are silent: a length beyond the table is clamped
 (page "Attention and KV Cache", Split keys, paged keys and the live length),
 rows with ``pos < 0`` see nothing, and ``causal = False`` makes every ``j < L``
 visible.
+
+Two variants (page "32. Production attention kernels"):
+
+- Sliding window (One kernel for the whole batch, the listing's window mask
+  and the point on sliding windows): with ``window > 0`` a key also needs
+  ``j > pos - window``, i.e. a row sees at most its last ``window``
+  positions.  The same condition applies when ``causal = False`` (reading:
+  the window is a lower bound on key positions, independent of the upper
+  one).
+- Attention sinks (Stretch exercises, attention sinks): one logit ``sink_h``
+  per query head, in the units of the scaled scores, joins every softmax
+  denominator and contributes no value:
+  ``out = sum_J exp(x_j - M) v_j / (exp(sink_h - M) + sum_J exp(x_j - M))``
+  with ``M = max(sink_h, max_J x_j)``.  A row with no visible key is still
+  zero.
 """
 from __future__ import annotations
 
@@ -55,12 +70,12 @@ def _seq_meta(block_tables, context_lens, query_start_loc, page_size):
     return out
 
 
-def visible_keys(L: int, n: int, t: int, causal: bool) -> int:
+def visible_keys(L: int, n: int, t: int, causal: bool, window: int = 0) -> int:
     """Number of visible keys of token t of an n-token step over context L."""
-    if not causal:
-        return L
     pos = L - n + t
-    return max(0, min(L, pos + 1))
+    hi = L if not causal else max(0, min(L, pos + 1))
+    lo = max(0, pos - window + 1) if window > 0 else 0
+    return max(0, hi - lo)
 
 
 def _gather(pool: torch.Tensor, table_row: torch.Tensor, L: int) -> torch.Tensor:
@@ -74,7 +89,7 @@ def _gather(pool: torch.Tensor, table_row: torch.Tensor, L: int) -> torch.Tensor
 
 def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale,
                   causal: bool = True, tokens: Optional[Iterable[int]] = None,
-                  chunk: int = 1024) -> torch.Tensor:
+                  chunk: int = 1024, window: int = 0, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Gather-then-dense attention in float64.
 
     Follows page "paged-attn-xpu" (the dense reference that gathers each
@@ -84,7 +99,8 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
     ``chunk`` tokens only to bound memory; each row's result is the definition.
 
     Returns float64 ``[N, Hq, D]``.  If ``tokens`` is given only those flat
-    token rows are computed; the other rows are left at zero.
+    token rows are computed; the other rows are left at zero.  ``window`` and
+    ``sinks`` ([Hq] logits, or None) are the two variants of the module text.
     """
     N, Hq, D = q.shape
     Hkv = k_pool.shape[2]
@@ -94,6 +110,7 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
     sc = float(scale)
     out = torch.zeros(N, Hq, D, dtype=torch.float64)
     want = None if tokens is None else sorted(set(int(t) for t in tokens))
+    sk = None if sinks is None else sinks.to(torch.float64).reshape(Hq, 1)   # [Hq, 1]
     for b, (s0, n, L) in enumerate(_seq_meta(block_tables, context_lens, query_start_loc, ps)):
         if n <= 0:
             continue
@@ -117,13 +134,19 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
             vis = j[None, :] < L
             if causal:
                 vis = vis & (j[None, :] <= pos[:, None])       # [T, hi]
+            if window > 0:
+                vis = vis & (j[None, :] > pos[:, None] - window)
             vis = vis.unsqueeze(0).expand(Hq, -1, -1)
             x = torch.where(vis, x, torch.tensor(-math.inf, dtype=torch.float64))
             empty = ~vis.any(-1)                               # [Hq, T]
             m = x.max(-1).values
+            if sk is not None:
+                m = torch.where(empty, m, torch.maximum(m, sk))
             m = torch.where(empty, torch.zeros_like(m), m)
             w = torch.exp(x - m.unsqueeze(-1))                 # masked -> exp(-inf) = 0
             den = w.sum(-1)
+            if sk is not None:
+                den = den + torch.exp(sk - m)
             o = torch.matmul(w, Vh[:, :hi]) / torch.where(empty, torch.ones_like(den), den).unsqueeze(-1)
             o = torch.where(empty.unsqueeze(-1), torch.zeros_like(o), o)
             out[s0 + tc] = o.permute(1, 0, 2)
@@ -131,13 +154,14 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
 
 
 def brute_force(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale,
-                causal: bool = True) -> List[List[List[float]]]:
+                causal: bool = True, window: int = 0, sinks=None) -> List[List[List[float]]]:
     """Scalar-loop attention with every pool address computed from strides.
 
     Pure Python (``math.exp``, ``math.fsum``), for tiny inputs only.  Written
     from the definition alone: for each row, list the visible keys, form each
     score as an explicit sum of products, subtract the maximum, exponentiate,
-    normalise and take the weighted sum of value rows.
+    normalise and take the weighted sum of value rows.  A sink is one more
+    term of the denominator (and of the maximum) with no value row.
     """
     qa = q.to(torch.float64).contiguous()
     N, Hq, D = qa.shape
@@ -164,7 +188,8 @@ def brute_force(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, 
             pos = L - n + t
             for h in range(Hq):
                 g = h // rep
-                keys = [j for j in range(L) if (not causal) or j <= pos]
+                keys = [j for j in range(L)
+                        if ((not causal) or j <= pos) and (window <= 0 or j > pos - window)]
                 if not keys:
                     continue
                 xs = []
@@ -173,9 +198,10 @@ def brute_force(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, 
                     base = page * sP + (j % ps) * sS + g * sH
                     dot = math.fsum(qf[(i * Hq + h) * D + d] * kf[base + d] for d in range(D))
                     xs.append(float(scale) * dot)
-                mx = max(xs)
+                extra = [] if sinks is None else [float(sinks[h])]
+                mx = max(xs + extra)
                 ws = [math.exp(x - mx) for x in xs]
-                den = math.fsum(ws)
+                den = math.fsum(ws + [math.exp(e - mx) for e in extra])
                 for d in range(D):
                     acc = []
                     for w, j in zip(ws, keys):
@@ -187,7 +213,8 @@ def brute_force(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, 
 
 def split_combine_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale,
                       causal: bool = True, num_splits: Optional[int] = None,
-                      boundaries: Optional[Sequence[int]] = None) -> torch.Tensor:
+                      boundaries: Optional[Sequence[int]] = None, window: int = 0,
+                      sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Split-KV attention merged by log-sum-exp weights, in float64.
 
     Page "32. Production attention kernels", Long contexts: split the keys.
@@ -201,7 +228,9 @@ def split_combine_f64(q, k_pool, v_pool, block_tables, context_lens, query_start
     ``num_splits`` cuts the sequence's pages into that many page-aligned
     ranges of ``ceil(pages / num_splits)`` pages (the split sizing of that
     page's launcher); ``boundaries`` instead gives explicit key positions
-    (any cut points, page-aligned or not).
+    (any cut points, page-aligned or not).  A sink enters the merge as one
+    more range with ``lse = sink_h`` and a zero output; windowed keys are
+    masked inside each range.
     """
     N, Hq, D = q.shape
     Hkv = k_pool.shape[2]
@@ -229,6 +258,8 @@ def split_combine_f64(q, k_pool, v_pool, block_tables, context_lens, query_start
             j = torch.arange(lo, hi)
             x = sc * torch.matmul(Q, Kb[:, lo:hi].transpose(1, 2))     # [Hq, n, hi-lo]
             vis = (j[None, :] <= pos[:, None]) if causal else torch.ones(n, hi - lo, dtype=torch.bool)
+            if window > 0:
+                vis = vis & (j[None, :] > pos[:, None] - window)
             vis = vis.unsqueeze(0).expand(Hq, -1, -1)
             x = torch.where(vis, x, torch.tensor(-math.inf, dtype=torch.float64))
             empty = ~vis.any(-1)
@@ -240,6 +271,9 @@ def split_combine_f64(q, k_pool, v_pool, block_tables, context_lens, query_start
                                 m + torch.log(torch.where(empty, torch.ones_like(l), l)))
             parts.append(o_s)
             lses.append(lse_s)
+        if sinks is not None:
+            parts.append(torch.zeros(Hq, n, D, dtype=torch.float64))
+            lses.append(sinks.to(torch.float64).reshape(Hq, 1).expand(Hq, n))
         lse_all = torch.stack(lses)                             # [S, Hq, n]
         top = lse_all.max(0).values
         none = torch.isinf(top) & (top < 0)
