@@ -44,26 +44,42 @@ TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.js
 
 
 # ----------------------------------------------------------------------------- accounting
-def algorithmic_bytes(context_lens, query_lens, num_q_heads, num_kv_heads, head_dim, page_size, elem_bytes):
+def _key_range(L, n, window):
+    """Positions [lo, hi) some query row of the step can see (causal or not:
+    keys past L never exist; a sliding window drops keys before the first
+    row's window start)."""
+    L = max(0, L)
+    lo = max(0, L - n - window + 1) if window > 0 else 0
+    return lo, L
+
+
+def algorithmic_bytes(context_lens, query_lens, num_q_heads, num_kv_heads, head_dim, page_size, elem_bytes,
+                      window=0):
     """Bytes the method must move: K and V of every visible position once per
     GQA group, q read and out written once, the page ids of the pages used,
     the lengths and query offsets.  (Page "32. Production attention kernels",
-    What the reference backend costs: 2 x Hkv x D values per token per layer.)"""
-    kv = sum(max(0, L) for L in context_lens) * num_kv_heads * head_dim * 2 * elem_bytes
+    What the reference backend costs: 2 x Hkv x D values per token per layer.)
+    With a sliding window only the positions some row can see count."""
+    kv = ids = 0
+    for L, n in zip(context_lens, query_lens):
+        lo, hi = _key_range(L, n, window)
+        kv += (hi - lo) * num_kv_heads * head_dim * 2 * elem_bytes
+        ids += ((hi + page_size - 1) // page_size - lo // page_size) * 4 if hi > lo else 0
     n = sum(query_lens)
     qo = n * num_q_heads * head_dim * elem_bytes * 2
-    ids = sum((max(0, L) + page_size - 1) // page_size for L in context_lens) * 4
     meta = (2 * len(context_lens) + 1) * 4
     return kv + qo + ids + meta
 
 
-def algorithmic_flops(context_lens, query_lens, num_q_heads, head_dim, causal=True):
+def algorithmic_flops(context_lens, query_lens, num_q_heads, head_dim, causal=True, window=0):
     """4 * D * Hq per visible (query, key) pair: 2 for q.k and 2 for p.v."""
     pairs = 0
     for L, n in zip(context_lens, query_lens):
         for t in range(n):
             pos = L - n + t
-            pairs += max(0, min(L, pos + 1)) if causal else L
+            hi = max(0, min(L, pos + 1)) if causal else max(0, L)
+            lo = max(0, pos - window + 1) if window > 0 else 0
+            pairs += max(0, hi - lo)
     return 4 * head_dim * num_q_heads * pairs
 
 
@@ -140,17 +156,6 @@ class DecodeBench:
         k, v = self.pools[layer % len(self.pools)]
         self.pa.kv_cache_write(self.k_new, self.v_new, k, v, self.slots)
 
-    def parity(self, seqs=(0, 17, 63)):
-        """Sampled check of layer 0 against the oracle, before any write."""
-        from oracle import attention_f64
-        torch = self.torch
-        out = self.attend(0).cpu()
-        toks = list(seqs)
-        w = self.w
-        ref = attention_f64(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
-                            tokens=toks)
-        idx = torch.tensor(toks)
-        return torch.max(torch.abs(out.index_select(0, idx).double() - ref.index_select(0, idx))).item()
 
 
 class PrefillBench:
@@ -193,12 +198,16 @@ class PrefillBench:
 class WorkloadBench:
     """Any seeded workload on device, pools rotated over `layers` sets."""
 
-    def __init__(self, config, layers=1):
+    def __init__(self, config, layers=1, window=0, sinks=False):
         import torch
         import paged_kv_attention_amd as pa
         from workloads import make
         self.torch, self.pa = torch, pa
         self.w = w = make(config)
+        self.window = window
+        # sink logits: one per query head, drawn from their own seeded stream
+        self.sinks_cpu = (torch.randn(w.num_q_heads, generator=torch.Generator().manual_seed(777)) * 2.0
+                          if sinks else None)
         dev = torch.device("cuda", 0)
         self.q = w.q.to(dev)
         self.bt = w.block_tables.to(dev)
@@ -219,24 +228,19 @@ class WorkloadBench:
         self.splits = pa.choose_splits(dims)
         lens = w.context_lens.tolist()
         e = 4 if w.dtype == torch.float32 else 2
-        self.bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, ps, e)
-        self.flops = algorithmic_flops(lens, w.query_lens, w.num_q_heads, w.head_dim)
+        self.bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, ps, e,
+                                       window=window)
+        self.flops = algorithmic_flops(lens, w.query_lens, w.num_q_heads, w.head_dim, causal=w.causal,
+                                       window=window)
+        self.sinks = None if self.sinks_cpu is None else self.sinks_cpu.to(dev)
 
     def attend(self, layer):
         k, v = self.pools[layer % len(self.pools)]
         w = self.w
         return self.pa.paged_attention(self.q, k, v, self.bt, self.cl, self.qsl, w.scale, w.causal, out=self.out,
-                                       workspace=self.ws, max_query_len=w.max_query_len)
+                                       workspace=self.ws, max_query_len=w.max_query_len, window=self.window,
+                                       sinks=self.sinks)
 
-    def parity(self, tokens):
-        from oracle import attention_f64
-        torch = self.torch
-        out = self.attend(0).cpu()
-        w = self.w
-        ref = attention_f64(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
-                            tokens=tokens)
-        idx = torch.tensor(tokens)
-        return torch.max(torch.abs(out.index_select(0, idx).double() - ref.index_select(0, idx))).item()
 
 
 def other_workloads(steps, warmup):
@@ -250,16 +254,47 @@ def other_workloads(steps, warmup):
                               (4, 8, "bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify")]:
         print(f"[bench] other workload {cfg}: building inputs", file=sys.stderr, flush=True)
         wb = WorkloadBench(cfg, layers)
-        qsl = wb.w.query_start_loc.tolist()
-        toks = sorted(set([0, qsl[-1] - 1] + [qsl[b] for b in range(0, wb.w.num_seqs, 7)]))
-        err = wb.parity(toks)
         _, per = _time_steps([wb.attend], steps, warmup)
         ms = per[0]
-        entry = {"workload": name, "ms": round(ms, 5), "splits": wb.splits, "parity_max_abs_err": err,
+        entry = {"workload": name, "ms": round(ms, 5), "splits": wb.splits,
                  "algorithmic_bytes": wb.bytes, "GB_s": round(wb.bytes / (ms * 1e-3) / 1e9, 2),
                  "hbm_frac": round(wb.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "algorithmic_flops": wb.flops, "pool_sets_rotated": layers}
         res[f"config{cfg}"] = entry
+        del wb
+        torch.cuda.empty_cache()
+    return res
+
+
+def variant_workloads(steps, warmup):
+    """The sliding-window and attention-sink variants at the headline shapes:
+    the 64 x 4096 decode with a 1024-position window (HBM-bound: only the
+    window's K/V count) and the 4 x 8192 causal prefill with a 4096-position
+    window (MFMA-bound: only the band's pairs count), both with one sink
+    logit per query head."""
+    import torch
+    res = {}
+    for cfg, layers, window, bound, name in [
+            (3, 4, 1024, "hbm", "bf16 decode 64 x 4096, 32/8 heads, D 128, page 64, window 1024, sinks"),
+            (5, 1, 4096, "mfma", "bf16 causal prefill 4 x 8192, 32/8 heads, D 128, page 64, window 4096, sinks")]:
+        print(f"[bench] variant: {name}", file=sys.stderr, flush=True)
+        wb = WorkloadBench(cfg, layers, window=window, sinks=True)
+        vsteps = steps if bound == "hbm" else max(3, min(steps, 10))
+        _, per = _time_steps([wb.attend], vsteps, warmup)
+        ms = per[0]
+        entry = {"workload": name, "ms": round(ms, 5), "window": window, "splits": wb.splits,
+                 "algorithmic_bytes": wb.bytes, "algorithmic_flops": wb.flops, "pool_sets_rotated": layers}
+        if bound == "hbm":
+            gbs = wb.bytes / (ms * 1e-3) / 1e9
+            entry.update({"GB_s": round(gbs, 2), "roofline": {"bound": "hbm", "achieved": round(gbs, 2),
+                                                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                              "frac": round(gbs / HBM_PEAK_GBS, 4)}})
+        else:
+            tf = wb.flops / (ms * 1e-3) / 1e12
+            entry.update({"TFLOP_s": round(tf, 2), "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                                                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                                                "frac": round(tf / BF16_PEAK_TFLOPS, 4)}})
+        res[f"config{cfg}_window{window}_sinks"] = entry
         del wb
         torch.cuda.empty_cache()
     return res
@@ -361,6 +396,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the other measured workloads")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay of the decode step")
+    ap.add_argument("--no-variants", action="store_true", help="skip the sliding-window / sink workloads")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -392,8 +428,6 @@ def main():
     if args.only in (None, "decode"):
         print("[bench] decode: building inputs", file=sys.stderr, flush=True)
         db = DecodeBench(layers=args.layers, num_splits=args.num_splits)
-        err = db.parity()
-        print(f"[bench] decode parity (3 sampled sequences): max abs err {err:.3e}", file=sys.stderr, flush=True)
         total, per = _time_steps([db.write, db.attend], args.steps, args.warmup)
         ms = total / args.steps
         value = db.attn_bytes / (ms * 1e-3) / 1e9
@@ -415,7 +449,6 @@ def main():
                          "kernel": "decode_splitkv_kernel<128,1>", "kernel_ms": round(kern_ms, 5),
                          "bytes_per_launch": db.attn_bytes},
             "kv_write_ms": round(per[0], 5),
-            "parity_max_abs_err": err,
         })
         if not args.no_graph:
             g_ms = graph_step(db, args.steps)
@@ -456,6 +489,9 @@ def main():
 
     if args.only is None and not args.no_others:
         result["other_workloads"] = other_workloads(args.steps, args.warmup)
+
+    if args.only is None and not args.no_variants:
+        result["variants"] = variant_workloads(args.steps, args.warmup)
 
     if not args.no_cpu_baseline and args.only is None and decode_w is not None:
         print("[bench] cpu baseline: timing the float64 oracle", file=sys.stderr, flush=True)

@@ -117,6 +117,44 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
                           const pa_dims* dims, pa_dtype dtype, void* stream);
 
 /*
+ * Options of paged_attention_opts.  Zero-initialise the struct and set the
+ * fields you use; a NULL options pointer means all defaults.
+ *
+ *   window  Sliding window (page "32. Production attention kernels", One
+ *           kernel for the whole batch: the window mask and the point on
+ *           sliding windows): when > 0, key j is visible to the query at
+ *           position pos only if also j > pos - window, so a row sees at most
+ *           its last `window` positions.  The condition applies with and
+ *           without `causal`.  0 = no window; negative is PA_ERR_SHAPE.
+ *   sinks   Attention sinks (same page, Stretch exercises: one learned logit
+ *           per head joins every softmax denominator and contributes no
+ *           value): device float32 [Hq], sink_h in the units of the scaled
+ *           scores scale * q.k.  Row (i, h) becomes
+ *           sum_J exp(x_j - M) v_j / (exp(sink_h - M) + sum_J exp(x_j - M)),
+ *           M = max(sink_h, max_J x_j); a row with no visible key stays zero.
+ *           NULL = no sinks.  Must be 4-byte aligned.
+ */
+typedef struct pa_attn_opts {
+  int32_t window;
+  int32_t reserved0;       /* must be 0 */
+  const float* sinks;
+} pa_attn_opts;
+
+/*
+ * paged_attention_opts -- paged_attention with the options above.  Every
+ * other argument, the layouts and the error behaviour are those of
+ * paged_attention, which is this call with opts == NULL.  The workspace
+ * pa_workspace_size(dims, dtype) returns is enough for any options (a window
+ * only lowers the split count).
+ */
+pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               const int32_t* query_start_loc, float scale, int causal,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               const pa_dims* dims, pa_dtype dtype, const pa_attn_opts* opts,
+                               void* stream);
+
+/*
  * kv_cache_write -- scatter new K/V rows into the pools.
  *
  * Token i's rows k_new[i, :, :] and v_new[i, :, :] ([num_tokens, Hkv, D] with

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_INVALID_DATA = range(7)
 PA_F32, PA_BF16 = 0, 1
 
-EXPORTED = ("paged_attention", "kv_cache_write", "pa_workspace_size", "pa_choose_splits", "pa_validate",
-            "pa_status_string", "pa_device_cu_count")
+EXPORTED = ("paged_attention", "paged_attention_opts", "kv_cache_write", "pa_workspace_size", "pa_choose_splits",
+            "pa_validate", "pa_status_string", "pa_device_cu_count")
 
 
 class PaDims(ctypes.Structure):
@@ -34,6 +34,10 @@ class PaDims(ctypes.Structure):
         ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
         ("kv_stride_page", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
     ]
+
+
+class PaAttnOpts(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("sinks", ctypes.c_void_p)]
 
 
 class PagedAttnError(RuntimeError):
@@ -58,6 +62,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention.restype = ctypes.c_int
     lib.paged_attention.argtypes = [vp, vp, vp, i32p, i32p, i32p, ctypes.c_float, ctypes.c_int, vp, vp,
                                     ctypes.c_size_t, ctypes.POINTER(PaDims), ctypes.c_int, vp]
+    lib.paged_attention_opts.restype = ctypes.c_int
+    lib.paged_attention_opts.argtypes = [vp, vp, vp, i32p, i32p, i32p, ctypes.c_float, ctypes.c_int, vp, vp,
+                                         ctypes.c_size_t, ctypes.POINTER(PaDims), ctypes.c_int,
+                                         ctypes.POINTER(PaAttnOpts), vp]
     lib.kv_cache_write.restype = ctypes.c_int
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.POINTER(PaDims), ctypes.c_int, vp]
@@ -165,11 +173,15 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                     context_lens: torch.Tensor, query_start_loc: torch.Tensor, scale: Optional[float] = None,
                     causal: bool = True, *, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, max_query_len: Optional[int] = None,
-                    num_splits: int = 0, stream=None) -> torch.Tensor:
+                    num_splits: int = 0, window: int = 0, sinks: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
     """Causal GQA attention of q over the paged pools; returns ``out`` [N, Hq, D].
 
     ``scale`` defaults to 1/sqrt(D).  ``max_query_len`` is a host bound on any
     sequence's query tokens (default N); ``num_splits`` 0 picks the split count.
+    ``window`` > 0 is a sliding window (a row sees its last ``window``
+    positions) and ``sinks`` a float32 [Hq] device tensor of sink logits; with
+    either set the call goes through ``paged_attention_opts``.
     """
     lib = load_library()
     if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
@@ -190,9 +202,20 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    st = lib.paged_attention(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), bt.data_ptr(), cl.data_ptr(),
-                             qsl.data_ptr(), float(scale), 1 if causal else 0, out.data_ptr(), ws_ptr, ws_bytes,
-                             ctypes.byref(dims), code, _stream_ptr(stream))
+    if window or sinks is not None:
+        if sinks is not None:
+            if sinks.dtype != torch.float32 or sinks.device != q.device or sinks.numel() != q.shape[1]:
+                raise ValueError("sinks must be a float32 tensor of num_q_heads values on q's device")
+            sinks = sinks.contiguous()
+        opts = PaAttnOpts(int(window), 0, sinks.data_ptr() if sinks is not None else None)
+        st = lib.paged_attention_opts(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), bt.data_ptr(),
+                                      cl.data_ptr(), qsl.data_ptr(), float(scale), 1 if causal else 0,
+                                      out.data_ptr(), ws_ptr, ws_bytes, ctypes.byref(dims), code,
+                                      ctypes.byref(opts), _stream_ptr(stream))
+    else:
+        st = lib.paged_attention(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), bt.data_ptr(), cl.data_ptr(),
+                                 qsl.data_ptr(), float(scale), 1 if causal else 0, out.data_ptr(), ws_ptr, ws_bytes,
+                                 ctypes.byref(dims), code, _stream_ptr(stream))
     if st != PA_OK:
         raise PagedAttnError(st, "paged_attention")
     return out

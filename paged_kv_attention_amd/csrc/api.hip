@@ -117,13 +117,25 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
                           void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims, pa_dtype dtype,
                           void* stream) {
+  return paged_attention_opts(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale, causal, out,
+                              workspace, workspace_bytes, dims, dtype, nullptr, stream);
+}
+
+pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
+                               void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims,
+                               pa_dtype dtype, const pa_attn_opts* opts, void* stream) {
   pa_status st = check_dims(dims, dtype);
   if (st != PA_OK) return st;
   if (!isfinite(scale)) return PA_ERR_SHAPE;
+  const int window = opts ? opts->window : 0;
+  const float* sinks = opts ? opts->sinks : nullptr;
+  if (window < 0 || (opts && opts->reserved0 != 0)) return PA_ERR_SHAPE;
+  if (sinks && ((uintptr_t)sinks & 3u)) return PA_ERR_UNSUPPORTED;
   if (dims->num_seqs == 0 || dims->num_tokens == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start_loc || !out) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_UNSUPPORTED;
-  const Plan pl = make_plan(dims, dtype, cu_count());
+  const Plan pl = make_plan(dims, dtype, cu_count(), window);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
 
@@ -170,6 +182,8 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
   p.ws_tok = pl.ws_tok;
   p.comb_splits_small = pl.dec_small || dtype == PA_F32 ? pl.splits : 1;
   p.comb_splits_big = pl.dec_big || dtype == PA_F32 ? pl.splits_big : 1;
+  p.window = pl.window;
+  p.sinks = sinks;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;

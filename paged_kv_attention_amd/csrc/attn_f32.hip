@@ -8,7 +8,10 @@
 // with the chunk's probabilities read lane by lane.  Everything stays float32
 // (page "paged-attn-xpu", Requirements and limits: scores and softmax state
 // float32, split partials float32) and only keys below the row's visible end
-// are ever read, so slots past the context are never touched.
+// are ever read, so slots past the context are never touched.  With a
+// sliding window a row also starts at its own window start; split 0 folds an
+// attention sink into its state as one more score with no value row (page
+// "32. Production attention kernels", window mask and Stretch exercises).
 #include "pa_device.h"
 
 namespace pa {
@@ -34,8 +37,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
   const int kend = p.causal ? clampi(L - n + t + 1, 0, L) : L;
   const int kpp = p.pages_per_split * ps;
-  const int k_begin = split * kpp;
-  const int k_stop = min(k_begin + kpp, kend);
+  // splits cut the pages from the sequence's first window start (page 0
+  // without a window); this row reads only its own window
+  const int k_split = (split_page_base(L, n, p.window, ps) + split * p.pages_per_split) * ps;
+  const int k_begin = p.window > 0 ? max(k_split, L - n + t - p.window + 1) : k_split;
+  const int k_stop = min(k_split + kpp, kend);
   const int g = h / p.group;
   const int tok = s0 + t;
 
@@ -89,6 +95,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     }
   }
 
+  if (p.sinks && split == 0) {
+    // the sink joins split 0 as one more score with no value row
+    const float s2 = p.sinks[h] * kLog2e;
+    const float mn = fmaxf(m_run, s2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float e = fast_exp2(m_run - ms);
+    l_run = l_run * e + fast_exp2(s2 - ms);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] *= e;
+    m_run = mn;
+  }
   const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
   if (S == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;

@@ -28,11 +28,20 @@
 // NaN in an unused slot cannot reach an output (page "Attention and KV
 // Cache", live length: a true select, not a multiply by zero).
 //
+// Sliding window (page "32. Production attention kernels", the unified
+// kernel's window mask): the splits cut the pages from the first token's
+// window start, chunks start at that start's 16-key tile, and chunks that
+// reach below the last token's window start are masked per row.  Attention
+// sinks (same page, Stretch exercises): split 0 folds the head's sink logit
+// into its merged state as one more score with no value row.
+//
 // The four waves' states are merged in LDS in a fixed order.  With one split
 // the normalised output is written directly; otherwise the unnormalised
 // partial (acc, m, l) goes to the float32 workspace for the combine kernel,
 // and a split without keys writes the neutral (0, -inf, 0) (page "Attention
 // and KV Cache", Split-KV decode).
+#include <limits.h>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -65,7 +74,9 @@ struct DecodeChunk {
   u32x4 v[DecodeCfg<D>::VLOADS];
 };
 
-template <int D, int NT>
+// WIN: the launch has a sliding window (p.window > 0); SINK: sink logits
+// (p.sinks != null).  The plain instantiation carries none of their code.
+template <int D, int NT, bool WIN, bool SINK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D>;
   constexpr int ROWS = 16 * NT;
@@ -85,15 +96,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int ps = p.page_size;
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
   const int npages = (L + ps - 1) / ps;
-  const int pg0 = split * p.pages_per_split;
+  const int window = WIN ? p.window : 0;
+  // with a sliding window the splits cut the pages from the first token's
+  // window start on, and keys below that start are never loaded
+  const int pg0 = (WIN ? split_page_base(L, n, window, ps) : 0) + split * p.pages_per_split;
   const int pg1 = min(pg0 + p.pages_per_split, npages);
-  const int k_begin = pg0 * ps;
+  const int wlo = WIN ? max(0, L - n - window + 1) : 0;
+  const int k_begin = WIN ? max(pg0 * ps, wlo & ~15) : pg0 * ps;   // 16-key tiles stay inside pages
   const int k_end = min(pg1 * ps, L);
   const int nchunks = k_end > k_begin ? (k_end - k_begin + C::KC - 1) / C::KC : 0;
   const int causal = p.causal;
   const int diag = L - n;                       // token t sees keys j <= diag + t
-  // keys below mask_lim are visible to every row of this tile
+  // keys below mask_lim are visible to every row of this tile, and so are
+  // keys at or above win_all (inside the last token's window)
   const int mask_lim = min(k_end, causal ? diag + 1 : L);
+  const int win_all = WIN ? diag + n - window : INT_MIN;
 
   // ---- query tile as the B operand of S^T = K . Q^T (row = lane % 16)
   bf16x8 qB[NT][C::DS];
@@ -156,14 +173,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 
   auto process = [&](int c, const DecodeChunk<D>& ch) {
     const int k0 = k_begin + c * C::KC;
-    const bool need_mask = k0 + C::KC > mask_lim;
-    // V chunk -> this wave's LDS tile, rows past the split's end selected to zero
+    const bool need_mask = k0 + C::KC > mask_lim || k0 < win_all;
+    // V chunk -> this wave's LDS tile; rows past the split's end or before
+    // every row's window are selected to zero
 #pragma unroll
     for (int i = 0; i < C::VLOADS; ++i) {
       const int idx = i * 64 + lane;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       u32x4 v = ch.v[i];
-      if (need_mask && k0 + kl >= k_end) v = u32x4{0u, 0u, 0u, 0u};
+      if (need_mask && (k0 + kl >= k_end || (WIN && k0 + kl < wlo))) v = u32x4{0u, 0u, 0u, 0u};
       *(PA_LDS u32x4*)(vl + kl * C::ROW_BYTES + cc * 16) = v;
     }
     // S^T = K . Q^T
@@ -189,7 +207,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
           float v = st[t][nt][r] * p.scale_log2;
           if (need_mask) {
             const int j = k0 + 16 * t + 4 * q4 + r;
-            const bool vis = j < k_end && (!causal || j <= diag + tok);
+            const bool vis = j < k_end && (!causal || j <= diag + tok) && (!WIN || j > diag + tok - window);
             v = vis ? v : kNegInf;
           }
           x[t][r] = v;
@@ -294,9 +312,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   for (int it = threadIdx.x; it < nrows * (D / 4); it += 256) {
     const int row = it / (D / 4), c4 = it % (D / 4);
     const int tok = s0 + row / G, head = g * G + row % G;
-    const float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
-    const float Lt = ((Lw[row] + Lw[ROWS + row]) + Lw[2 * ROWS + row]) + Lw[3 * ROWS + row];
-    const f32x4 o = *(const f32x4*)(Ob + row * ORS + 4 * c4);
+    float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
+    float Lt = ((Lw[row] + Lw[ROWS + row]) + Lw[2 * ROWS + row]) + Lw[3 * ROWS + row];
+    f32x4 o = *(const f32x4*)(Ob + row * ORS + 4 * c4);
+    if (SINK && split == 0) {
+      // the sink joins split 0 as one more score with no value row
+      const float s2 = p.sinks[head] * kLog2e;
+      const float Mn = fmaxf(M, s2);
+      const float Ms = Mn == kNegInf ? 0.f : Mn;
+      const float e = fast_exp2(M - Ms);
+      Lt = Lt * e + fast_exp2(s2 - Ms);
+      o *= e;
+      M = Mn;
+    }
     if (p.num_splits == 1) {
       const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
@@ -312,7 +340,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 template <int D, int NT>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
-  hipLaunchKernelGGL((decode_splitkv_kernel<D, NT>), grid, dim3(256), 0, st, p);
+  const bool win = p.window > 0, sink = p.sinks != nullptr;
+  if (win && sink)
+    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, true>), grid, dim3(256), 0, st, p);
+  else if (win)
+    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, false>), grid, dim3(256), 0, st, p);
+  else if (sink)
+    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, true>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, false>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -47,7 +47,11 @@ pa_status check_dims(const pa_dims* d, pa_dtype dtype) {
 }
 
 int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count) {
-  const int W = d->table_width > 0 ? d->table_width : 1;
+  return choose_splits_over(d, dtype, cu_count, d->table_width > 0 ? d->table_width : 1);
+}
+
+int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W) {
+  if (W < 1) W = 1;
   if (d->num_splits > 0) return d->num_splits < W ? d->num_splits : W;
   if (cu_count < 1) cu_count = 1;
   // units of parallel work per split: (sequence, KV head) workgroups of 4 waves
@@ -68,13 +72,24 @@ int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count) {
   return (int)s;
 }
 
-Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count) {
+int window_pages(int window, int mql, int page_size, int W) {
+  if (window <= 0) return W;
+  // keys a sequence's step can see: from its first token's window start to
+  // its last token, at most window + mql - 1 of them, over at most two more
+  // pages than they fill
+  const int64_t span = ((int64_t)window + (mql > 0 ? mql : 1) - 1) / page_size + 2;
+  return span < W ? (int)span : W;
+}
+
+Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
   Plan pl{};
   const int N = d->num_tokens;
   const int G = d->num_q_heads / d->num_kv_heads;
-  const int W = d->table_width > 0 ? d->table_width : 1;
   pl.mql = d->max_query_len > 0 && d->max_query_len < N ? d->max_query_len : N;
-  int S = choose_splits(d, dtype, cu_count);
+  // with a sliding window the splits cut the window's pages, not the table
+  const int W = window_pages(window, pl.mql, d->page_size, d->table_width > 0 ? d->table_width : 1);
+  pl.window = window > 0 ? window : 0;
+  int S = choose_splits_over(d, dtype, cu_count, W);
   pl.pages_per_split = (W + S - 1) / S;
   pl.splits = (W + pl.pages_per_split - 1) / pl.pages_per_split;
   if (dtype == PA_BF16) {

@@ -28,6 +28,7 @@ struct Plan {
   int comb_max_n;          // combine: sequences with n <= comb_max_n
   int ws_tok;              // workspace row slots per sequence
   size_t workspace_bytes;  // bytes the call needs
+  int window;              // sliding window (0 = none): splits cut the window's pages
 };
 
 // Checks dims and dtype; PA_OK or the error status (nothing else is touched).
@@ -37,9 +38,17 @@ pa_status check_dims(const pa_dims* d, pa_dtype dtype);
 // CUs about twice, at least 256 keys per split, at most 32 splits; an
 // explicit dims->num_splits > 0 wins (capped at W).
 int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count);
+// The same rule over W pages instead of the table width.
+int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W);
 
-// Full launch plan for valid dims (call check_dims first).
-Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count);
+// Pages a split range must cover: the table width W, or with a sliding window
+// (window > 0) the pages from a step's first window start to its end.
+int window_pages(int window, int mql, int page_size, int W);
+
+// Full launch plan for valid dims (call check_dims first).  With window > 0
+// the splits cut window_pages() pages starting at the page of the first
+// token's window start (the kernels find that page from the device lengths).
+Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window = 0);
 
 // Host-side check of copied metadata (the body of pa_validate).
 pa_status validate_host(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,

@@ -22,6 +22,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 #define PA_LDS __attribute__((address_space(3)))
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;   // log2(e): natural-log logits to exp2 units
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -40,7 +40,17 @@ struct AttnParams {
   int32_t comb_tokens;      // combine: token slots per sequence in the grid
   int32_t comb_splits_small;  // combine: splits of rows with n*G <= 16 (1 = written by the decode kernel)
   int32_t comb_splits_big;    // combine: splits of rows with n*G > 16
+  int32_t window;           // sliding window: key j visible to position pos only if j > pos - window (0 = none)
+  const float* sinks;       // [Hq] sink logits in scaled-score units, or null
 };
+
+// First page of the split ranges of a sequence with context L and n step
+// tokens: the page of its first token's window start (0 without a window).
+constexpr int split_page_base(int L, int n, int window, int page_size) {
+  if (window <= 0) return 0;
+  const int lo = L - n - window + 1;
+  return lo > 0 ? lo / page_size : 0;
+}
 
 struct KvWriteParams {
   const void* k_new;

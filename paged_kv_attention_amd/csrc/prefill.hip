@@ -26,12 +26,21 @@
 //   P rounded to bf16 (same passage), its row sum taken from the rounded
 //   values, O^T[D x 32 rows] += V^T . P^T on MFMA with V^T read transposed from
 //   LDS (ds_read_b64_tr_b16) and P^T taken straight from the S^T accumulator.
-// Keys past the context end are zero-filled in LDS and never loaded.
+// Keys past the context end, and keys before the tile's first window start,
+// are zero-filled in LDS and never loaded.
+//
+// With a sliding window (page "32. Production attention kernels", the unified
+// kernel's window mask) the key loop starts at the block holding the tile's
+// first window start and masks the blocks below its last one; an attention
+// sink (same page, Stretch exercises) is folded into each row's state before
+// the normalisation, as one more score with no value row.
 //
 // Tiles with more keys run first (page "Attention kernels", Open questions:
 // heaviest causal blocks first), and the flat block index is remapped so
 // that the tiles of one (sequence, KV head) land on the same XCD and share
 // its L2.
+#include <limits.h>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -61,7 +70,9 @@ struct PrefillRegs {
   u32x4 k[PrefillCfg<D, NW, 1, KB>::LOADS], v[PrefillCfg<D, NW, 1, KB>::LOADS];
 };
 
-template <int D, int NW, int PF, int KB>
+// WIN: the launch has a sliding window (p.window > 0); the windowless
+// instantiation carries none of its bounds or masks.
+template <int D, int NW, int PF, int KB, bool WIN>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void prefill_kernel(const AttnParams p) {
   using C = PrefillCfg<D, NW, PF, KB>;
@@ -95,6 +106,12 @@ void prefill_kernel(const AttnParams p) {
   const int k_hi = causal ? clampi(diag + t0 + tcount, 0, L) : L;   // keys any row can see
   const int full_lim = causal ? clampi(diag + t0 + 1, 0, L) : L;    // keys every row sees
   const int nblk = (k_hi + C::KB - 1) / C::KB;
+  // sliding window: blocks before the first row's window start are skipped,
+  // and keys below the last row's window start need the window mask
+  const int window = WIN ? p.window : 0;
+  const int wlo_tile = WIN ? max(0, diag + t0 - window + 1) : 0;   // first row's window start
+  const int blk0 = wlo_tile / C::KB;
+  const int win_all = WIN ? diag + t0 + tcount - window : INT_MIN;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, h2 = lane >> 5;
@@ -150,7 +167,7 @@ void prefill_kernel(const AttnParams p) {
       if (jw < L) {
         const int lp = jw >> psh;
         const int64_t pbase = (int64_t)page_of(p, b, lp) * p.kv_stride_page;
-        if (j < L) {
+        if (j < L && (!WIN || j >= wlo_tile)) {
           const int64_t off = pbase + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;
           r.k[i] = *(const u32x4*)(kbase + off);
           r.v[i] = *(const u32x4*)(vbase + off);
@@ -215,13 +232,13 @@ void prefill_kernel(const AttnParams p) {
   // Mask, online-softmax update and bf16 P^T of block blk.
   auto softmax = [&](int blk, f32x16 (&st)[C::KT], uint32_t (&pk)[C::KT][8]) {
     const int kb0 = blk * C::KB;
-    if (kb0 + C::KB > full_lim) {
+    if (kb0 + C::KB > full_lim || kb0 < win_all) {
 #pragma unroll
       for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb0 + 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          const bool vis = j < L && (!causal || j <= diag + my_tok);
+          const bool vis = j < L && (!causal || j <= diag + my_tok) && (!WIN || j > diag + my_tok - window);
           st[kt][r] = vis ? st[kt][r] : kNegInf;
         }
     }
@@ -235,8 +252,10 @@ void prefill_kernel(const AttnParams p) {
     // lazy rescale: move the reference max only when this block exceeds it by > TAU
     const bool need = m_blk > m_run + C::TAU;
     if (__builtin_amdgcn_ballot_w64(need)) {
+      // rows that keep their reference keep alpha = 1 (also while it is still
+      // -inf: a row whose window starts later has seen no key yet)
       const float m_upd = need ? m_blk : m_run;
-      const float alpha = fast_exp2(m_run - m_upd);   // 1 when unchanged, 0 from -inf
+      const float alpha = need ? fast_exp2(m_run - m_blk) : 1.f;   // 0 from -inf
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
@@ -281,15 +300,15 @@ void prefill_kernel(const AttnParams p) {
   f32x16 st[C::KT];
   uint32_t pk[C::KT][8];
   PrefillRegs<D, NW, KB> rg[PF];
-  if (nblk > 0) {
-    gload(0, rg[0]);
-    lstore(0, rg[0]);
+  if (blk0 < nblk) {
+    gload(blk0, rg[0]);
+    lstore(blk0 & 1, rg[0]);
 #pragma unroll
     for (int j = 0; j < PF; ++j)
-      if (1 + j < nblk) gload(1 + j, rg[j]);
+      if (blk0 + 1 + j < nblk) gload(blk0 + 1 + j, rg[j]);
   }
   __syncthreads();
-  for (int base = 0; base < nblk; base += PF) {
+  for (int base = blk0; base < nblk; base += PF) {
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       const int blk = base + k;
@@ -306,6 +325,16 @@ void prefill_kernel(const AttnParams p) {
 
   // ---- normalise and write this lane's row (dims 32*dt + 8*(r/4) + 4*h2 + r%4)
   l_run = xor32_sum(l_run);
+  if (p.sinks) {
+    // the row's sink is one more score with no value row
+    const float s2 = row_ok ? p.sinks[my_head] * kLog2e : kNegInf;
+    const float mn = fmaxf(m_run, s2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float e = fast_exp2(m_run - ms);
+    l_run = l_run * e + fast_exp2(s2 - ms);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= e;
+  }
   if (row_ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     __bf16* op = (__bf16*)p.out + (int64_t)(s0 + my_tok) * p.o_stride_tok + (int64_t)my_head * p.o_stride_head + 4 * h2;
@@ -335,7 +364,10 @@ template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
   constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF, KB = PrefillShape<D>::KB;
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs;
-  hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
+  if (p.window > 0)
+    hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def to_dev(w: Workload, layout: str = "head_major"):
 
 
 def run_lib(w: Workload, num_splits: int = 0, layout: str = "head_major", max_query_len: Optional[int] = None,
-            out_fill: Optional[float] = None) -> torch.Tensor:
+            out_fill: Optional[float] = None, window: int = 0, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     t = to_dev(w, layout)
     out = None
     if out_fill is not None:
@@ -34,7 +34,8 @@ def run_lib(w: Workload, num_splits: int = 0, layout: str = "head_major", max_qu
     out = pa.paged_attention(t["q"], t["k_pool"], t["v_pool"], t["block_tables"], t["context_lens"],
                              t["query_start_loc"], w.scale, w.causal, out=out,
                              max_query_len=max_query_len if max_query_len is not None else w.max_query_len,
-                             num_splits=num_splits)
+                             num_splits=num_splits, window=window,
+                             sinks=None if sinks is None else sinks.to(torch.float32).to(t["q"].device))
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -45,11 +46,12 @@ def covered_tokens(w: Workload):
 
 
 def check(w: Workload, got: torch.Tensor, tokens: Optional[Iterable[int]] = None, tol: Optional[float] = None,
-          label: str = "") -> float:
+          label: str = "", window: int = 0, sinks: Optional[torch.Tensor] = None) -> float:
     tol = TOL[w.dtype] if tol is None else tol
     toks = covered_tokens(w) if tokens is None else sorted(set(tokens))
     ref = attention_f64(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
-                        causal=w.causal, tokens=toks)
+                        causal=w.causal, tokens=toks, window=window,
+                        sinks=None if sinks is None else sinks.to(torch.float32).double())
     idx = torch.tensor(toks, dtype=torch.int64)
     g = got.index_select(0, idx).double()
     r = ref.index_select(0, idx)

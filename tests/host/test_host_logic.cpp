@@ -5,6 +5,7 @@
 #include <vector>
 
 #include "host_logic.h"
+#include "pa_params.h"
 
 static int failures = 0;
 #define CHECK(c) do { if (!(c)) { std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #c); ++failures; } } while (0)
@@ -29,6 +30,18 @@ int main() {
   pa::Plan p2 = pa::make_plan(&c2, PA_BF16, 256);
   CHECK(p2.splits == 2 && p2.pages_per_split == 32 && p2.combine && p2.comb_tokens == 1);
   CHECK(p2.workspace_bytes == (size_t)2 * 32 * 32 * 130 * 4);
+  // sliding window: the splits cut the window's pages, never more than the table's
+  CHECK(pa::window_pages(0, 1, 64, 64) == 64);
+  CHECK(pa::window_pages(1024, 1, 64, 64) == 18);          // 1024 keys over at most 18 pages
+  CHECK(pa::window_pages(100000, 1, 64, 64) == 64);
+  CHECK(pa::window_pages(1, 16, 16, 64) == 3);          // 16 keys straddle at most 2 pages; one spare
+  pa::Plan pw = pa::make_plan(&c2, PA_BF16, 256, 1024);
+  CHECK(pw.window == 1024 && pw.splits == 2 && pw.pages_per_split == 9);
+  CHECK(pw.workspace_bytes <= p2.workspace_bytes);
+  // split ranges start at the page of the first token's window start
+  CHECK(pa::split_page_base(4096, 1, 1024, 64) == 48 && pa::split_page_base(4096, 1, 0, 64) == 0);
+  CHECK(pa::split_page_base(100, 1, 1024, 64) == 0 && pa::split_page_base(1025, 1, 1024, 64) == 0);
+  CHECK(pa::split_page_base(1089, 1, 1024, 64) == 1);
   // mixed batch: prefill + small and large decode tiles
   pa_dims c4 = dims(32, 547, 512, 32, 8, 128, 64, 2000, 128);
   pa::Plan p4 = pa::make_plan(&c4, PA_BF16, 256);

@@ -7,7 +7,7 @@ import re
 import pytest
 
 import paged_kv_attention_amd as pa
-from paged_kv_attention_amd._lib import PaDims
+from paged_kv_attention_amd._lib import PaDims, PaAttnOpts
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedattn.h")
 
@@ -68,6 +68,21 @@ def test_argument_errors_return_status_without_launch():
     assert _call(_dims(num_seqs=0, num_tokens=0)) == pa.PA_OK              # nothing to do
     assert _call(_dims(num_q_heads=65 * 2, num_kv_heads=2, q_stride_tok=130 * 128, o_stride_tok=130 * 128)) \
         == pa.PA_ERR_UNSUPPORTED                                            # bf16 group > 64
+
+
+def test_option_errors_return_status_without_launch():
+    lib = pa.load_library()
+    p = ctypes.c_void_p(16)
+
+    def call(opts, d=None):
+        d = d or _dims()
+        return lib.paged_attention_opts(p, p, p, p, p, p, ctypes.c_float(0.088), 1, p, None, 0, ctypes.byref(d), 1,
+                                        None if opts is None else ctypes.byref(opts), None)
+    assert call(PaAttnOpts(-1, 0, None)) == pa.PA_ERR_SHAPE                 # negative window
+    assert call(PaAttnOpts(0, 5, None)) == pa.PA_ERR_SHAPE                  # reserved field set
+    assert call(PaAttnOpts(0, 0, 18)) == pa.PA_ERR_UNSUPPORTED              # sinks not 4-byte aligned
+    assert call(PaAttnOpts(0, 0, None), _dims(head_dim=96)) == pa.PA_ERR_UNSUPPORTED
+    assert call(PaAttnOpts(16, 0, None), _dims(num_seqs=0, num_tokens=0)) == pa.PA_OK
 
 
 def test_workspace_and_split_rules():

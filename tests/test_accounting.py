@@ -39,3 +39,23 @@ def test_prefill_flops_closed_form():
     assert bench.algorithmic_flops([10], [3], 1, 1, causal=False) == 4 * 30
     # an invalid step with more tokens than positions: early tokens see nothing
     assert bench.algorithmic_flops([2], [4], 1, 1) == 4 * (0 + 0 + 1 + 2)
+
+
+def test_window_bytes_and_flops_closed_forms():
+    # decode with a 1024-position window reads the last 1024 keys: 16 pages of 64
+    b = bench.algorithmic_bytes([4096] * 64, [1] * 64, 32, 8, 128, 64, 2, window=1024)
+    assert b == 64 * 1024 * 8 * 128 * 2 * 2 + 64 * 32 * 128 * 2 * 2 + 64 * 16 * 4 + 129 * 4
+    # a window starting mid-page still counts the page holding its first key
+    # (keys 50..99 span pages 0 and 1; keys 70..99 lie in page 1 only)
+    assert bench.algorithmic_bytes([100], [1], 1, 1, 8, 64, 2, window=50) == 50 * 8 * 2 * 2 + 8 * 2 * 2 + 2 * 4 + 12
+    assert bench.algorithmic_bytes([100], [1], 1, 1, 8, 64, 2, window=30) == 30 * 8 * 2 * 2 + 8 * 2 * 2 + 4 + 12
+    # a window wider than the context changes nothing
+    assert bench.algorithmic_bytes([300], [5], 4, 2, 64, 16, 2, window=1000) == \
+        bench.algorithmic_bytes([300], [5], 4, 2, 64, 16, 2)
+    # causal prefill n = L = 8192 with window 4096: rows 0..4095 see t + 1 keys, the rest 4096
+    L, W = 8192, 4096
+    pairs = W * (W + 1) // 2 + (L - W) * W
+    assert bench.algorithmic_flops([L] * 4, [L] * 4, 32, 128, window=W) == 4 * 128 * 32 * 4 * pairs
+    assert bench.algorithmic_flops([10], [3], 1, 1, window=2) == 4 * 6
+    # not causal: row at pos sees [pos - 1, 10), i.e. 4, 3 and 2 keys
+    assert bench.algorithmic_flops([10], [3], 1, 1, causal=False, window=2) == 4 * (4 + 3 + 2)
