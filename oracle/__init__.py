@@ -18,11 +18,19 @@ Functions (each cites the passage it follows in ``oracle/attention.py``):
 * ``split_combine_f64`` -- split-KV: per-split normalised output and
                            log-sum-exp, merged with weights exp(lse_s - lse).
 * ``kv_write_ref``      -- the slot-mapped scatter of new K/V rows into the pools.
+* ``quantize_kv``, ``kv_write_quant_ref``, ``dequantize`` (``oracle/kv_quant.py``)
+                        -- the quantized cache: one float32 scale per (token,
+                           KV head), int8 or fp8 E4M3 codes, optional key
+                           smoothing, and the exact float64 read-back.
 
 All three attention functions are pinned against brute force, a library special
-case, closed forms and invariants in ``tests/test_oracle.py``; no function here
-is "parity unpinned".
+case, closed forms and invariants in ``tests/test_oracle.py`` and
+``tests/test_oracle_window_sinks.py``; the quantizer against error bounds,
+printed figures and exhaustive code tables in ``tests/test_oracle_kv_quant.py``.
+No function here is "parity unpinned".
 """
 from .attention import attention_f64, brute_force, split_combine_f64, kv_write_ref, visible_keys
+from .kv_quant import KV_QMAX, KV_CODE_DTYPE, quantize_kv, kv_write_quant_ref, dequantize
 
-__all__ = ["attention_f64", "brute_force", "split_combine_f64", "kv_write_ref", "visible_keys"]
+__all__ = ["attention_f64", "brute_force", "split_combine_f64", "kv_write_ref", "visible_keys", "KV_QMAX",
+           "KV_CODE_DTYPE", "quantize_kv", "kv_write_quant_ref", "dequantize"]

@@ -1,0 +1,84 @@
+"""Quantized KV cache reference -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may use this module.  It imports nothing from the HIP library.
+
+What is computed (page "32. Production attention kernels", Quantized KV
+caches; page "Attention kernels", INT8 cache):
+
+* Quantize on write, one float32 scale per (token, KV head): for a head
+  vector x of D values (float32), ``amax = max(max_d |x_d|, 1e-8)``,
+  ``scale = amax / q_max`` with q_max = 127 (int8) or 448 (fp8 E4M3), and
+  ``codes = clamp(round_half_even(x / scale), -127, 127)`` as int8, or
+  ``x / scale`` converted to float8 E4M3 (round to nearest even; the largest
+  element lands on the code range's edge, so nothing overflows).  Every step
+  is a float32 operation in this order, so a kernel that takes the same steps
+  in float32 reproduces the codes and scales bit for bit.
+* Key smoothing (page "Attention kernels", INT8 cache: the queries are
+  multiplied by the keys' smoothing factors, which undoes the smoothing in the
+  scores): with per-channel factors ``smooth [Hkv, D]`` keys are divided by
+  them (float32) before quantization.  The key a cached code stands for is
+  then ``code * scale * smooth``, and the scores are unchanged:
+  ``q . (k / s * s) = (q * s) . (k / s)``.  No smoothing means factors of 1.
+* The cache is read back as ``code * scale`` (times ``smooth`` for keys),
+  exactly, in float64; attention over those dequantized values is the
+  target the quantized kernels are compared with (page "32. Production
+  attention kernels", The tests and the measurements: INT8 and FP8 caches
+  match the reference on the dequantized values).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["KV_QMAX", "KV_CODE_DTYPE", "quantize_kv", "kv_write_quant_ref", "dequantize"]
+
+KV_QMAX = {"int8": 127.0, "fp8": 448.0}
+KV_CODE_DTYPE = {"int8": torch.int8, "fp8": torch.float8_e4m3fn}
+
+
+def quantize_kv(x: torch.Tensor, kind: str, smooth: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """x [T, Hkv, D] -> (codes [T, Hkv, D] int8 / float8_e4m3fn, scales [T, Hkv] float32)."""
+    q_max = torch.tensor(KV_QMAX[kind], dtype=torch.float32)
+    xf = x.to(torch.float32)
+    if smooth is not None:
+        xf = xf / smooth.to(torch.float32).unsqueeze(0)        # [1, Hkv, D]
+    amax = xf.abs().amax(-1).clamp_min(torch.tensor(1e-8, dtype=torch.float32))
+    scale = amax / q_max
+    scaled = xf / scale.unsqueeze(-1)
+    if kind == "int8":
+        codes = scaled.round().clamp(-127, 127).to(torch.int8)
+    else:
+        codes = scaled.to(torch.float8_e4m3fn)
+    return codes, scale
+
+
+def kv_write_quant_ref(k_new, v_new, k_codes, v_codes, k_scale, v_scale, slot_mapping, kind: str,
+                       k_smooth: Optional[torch.Tensor] = None):
+    """Quantize token i's K/V head vectors and scatter codes and scales to
+    flat slot ``slot_mapping[i]`` (page s // ps, offset s % ps); -1 writes
+    nothing.  Code pools are [P, ps, Hkv, D], scale pools [P, ps, Hkv].
+    Returns new tensors; inputs are not modified."""
+    kc, ks = quantize_kv(k_new, kind, k_smooth)
+    vc, vs = quantize_kv(v_new, kind)
+    out = [t.clone() for t in (k_codes, v_codes, k_scale, v_scale)]
+    ps = out[0].shape[1]
+    for i, s in enumerate(slot_mapping.tolist()):
+        if s < 0:
+            continue
+        pg, sl = s // ps, s % ps
+        # copy through the bytes: a dtype is only an interpretation of them
+        out[0].view(torch.uint8)[pg, sl] = kc[i].view(torch.uint8)
+        out[1].view(torch.uint8)[pg, sl] = vc[i].view(torch.uint8)
+        out[2][pg, sl] = ks[i]
+        out[3][pg, sl] = vs[i]
+    return tuple(out)
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, smooth: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """codes [P, ps, Hkv, D], scales [P, ps, Hkv] -> float64 values code * scale (* smooth [Hkv, D])."""
+    v = codes.to(torch.float64) * scales.to(torch.float64).unsqueeze(-1)
+    if smooth is not None:
+        v = v * smooth.to(torch.float64).reshape(1, 1, *smooth.shape)
+    return v
