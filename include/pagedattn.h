@@ -117,6 +117,34 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
                           const pa_dims* dims, pa_dtype dtype, void* stream);
 
 /*
+ * Quantized KV cache (page "32. Production attention kernels", Quantized KV
+ * caches; page "Attention kernels", INT8 cache).  The pools hold 1-byte codes
+ * ([P, ps, Hkv, D] by the kv strides of pa_dims, which count bytes here) and
+ * one float32 scale per (page, slot, KV head) in two scale pools addressed by
+ * the strides below (in floats).  A cached value is code * scale; a cached
+ * key is code * scale * k_smooth[g][d] when smoothing factors are given.
+ *
+ * kv_cache_write_quant writes them: for each new head vector x (float32;
+ * keys first divided by k_smooth), amax = max(max |x|, 1e-8),
+ * scale = amax / q_max (127 int8, 448 fp8), codes = round-half-even(x / scale)
+ * clamped to [-127, 127] (int8) or x / scale converted to float8 E4M3 with
+ * round-to-nearest-even (fp8).  Every step is one float32 operation, so the
+ * codes and scales are reproducible bit for bit.
+ */
+typedef enum pa_kv_dtype { PA_KV_SAME = 0, PA_KV_INT8 = 1, PA_KV_FP8_E4M3 = 2 } pa_kv_dtype;
+
+typedef struct pa_kv_quant {
+  int32_t kv_dtype;            /* PA_KV_INT8 or PA_KV_FP8_E4M3                      */
+  int32_t reserved0;           /* must be 0                                          */
+  float* k_scale;              /* scale pools: one float32 per (page, slot, KV head) */
+  float* v_scale;
+  int64_t scale_stride_page;   /* float strides of both scale pools                  */
+  int64_t scale_stride_slot;
+  int64_t scale_stride_head;
+  const float* k_smooth;       /* [Hkv, D] float32 key smoothing factors, or NULL    */
+} pa_kv_quant;
+
+/*
  * Options of paged_attention_opts.  Zero-initialise the struct and set the
  * fields you use; a NULL options pointer means all defaults.
  *
@@ -133,11 +161,20 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
  *           sum_J exp(x_j - M) v_j / (exp(sink_h - M) + sum_J exp(x_j - M)),
  *           M = max(sink_h, max_J x_j); a row with no visible key stays zero.
  *           NULL = no sinks.  Must be 4-byte aligned.
+ *   kv_quant  Quantized pools (see pa_kv_quant), or NULL for pools in q's
+ *           element type.  Needs dtype PA_BF16 (PA_ERR_UNSUPPORTED
+ *           otherwise); the pools and kv strides must be 16-byte aligned in
+ *           bytes and the scale pools 4-byte aligned.  The codes are
+ *           converted to bf16 in registers, a key's scale multiplies its
+ *           scores and a value's scale its probability before the PV
+ *           product (decode and verification tiles); prefill tiles
+ *           dequantize into bf16 when a block is staged.
  */
 typedef struct pa_attn_opts {
   int32_t window;
   int32_t reserved0;       /* must be 0 */
   const float* sinks;
+  const pa_kv_quant* kv_quant;
 } pa_attn_opts;
 
 /*
@@ -170,6 +207,20 @@ pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, voi
                          const int32_t* slot_mapping, int32_t num_tokens,
                          int64_t new_stride_tok, int64_t new_stride_head,
                          const pa_dims* dims, pa_dtype dtype, void* stream);
+
+/*
+ * kv_cache_write_quant -- kv_cache_write into quantized pools: token i's K and
+ * V head vectors (new_dtype PA_BF16 or PA_F32, [num_tokens, Hkv, D] with the
+ * given element strides, D contiguous) are quantized as described above and
+ * their codes and scales go to flat slot slot_mapping[i]; -1 writes nothing
+ * and slots >= P*ps are skipped.  k_codes / v_codes are the code pools (kv
+ * strides of dims in bytes, 16-byte aligned), `quant` gives the scale pools
+ * and the optional key smoothing factors.
+ */
+pa_status kv_cache_write_quant(const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                               const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
+                               int64_t new_stride_head, const pa_dims* dims, pa_dtype new_dtype,
+                               const pa_kv_quant* quant, void* stream);
 
 /*
  * pa_workspace_size -- bytes of workspace paged_attention needs for these

@@ -8,10 +8,12 @@ The public functions marshal torch tensors into ``libpagedattn.so``:
 * ``workspace_size`` / ``choose_splits`` / ``validate`` -- planning and checks.
 """
 from ._lib import (PaDims, PagedAttnError, LIB_PATH, EXPORTED, load_library, paged_attention, kv_cache_write,
+                   kv_cache_write_quant, KvQuant, empty_code_pool, empty_scale_pool,
                    workspace_size, choose_splits, validate, make_dims, status_string, device_cu_count, empty_pool, pool_like,
                    PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH,
                    PA_ERR_INVALID_DATA)
 
 __all__ = ["PaDims", "PagedAttnError", "LIB_PATH", "EXPORTED", "load_library", "paged_attention", "kv_cache_write",
+           "kv_cache_write_quant", "KvQuant", "empty_code_pool", "empty_scale_pool",
            "workspace_size", "choose_splits", "validate", "make_dims", "status_string", "device_cu_count",
            "empty_pool", "pool_like"]

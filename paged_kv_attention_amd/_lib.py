@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_INVALID_DATA = range(7)
 PA_F32, PA_BF16 = 0, 1
 
-EXPORTED = ("paged_attention", "paged_attention_opts", "kv_cache_write", "pa_workspace_size", "pa_choose_splits",
-            "pa_validate", "pa_status_string", "pa_device_cu_count")
+EXPORTED = ("paged_attention", "paged_attention_opts", "kv_cache_write", "kv_cache_write_quant", "pa_workspace_size",
+            "pa_choose_splits", "pa_validate", "pa_status_string", "pa_device_cu_count")
 
 
 class PaDims(ctypes.Structure):
@@ -36,8 +36,66 @@ class PaDims(ctypes.Structure):
     ]
 
 
+class PaKvQuant(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("scale_stride_page", ctypes.c_int64),
+                ("scale_stride_slot", ctypes.c_int64), ("scale_stride_head", ctypes.c_int64),
+                ("k_smooth", ctypes.c_void_p)]
+
+
 class PaAttnOpts(ctypes.Structure):
-    _fields_ = [("window", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("sinks", ctypes.c_void_p)]
+    _fields_ = [("window", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("sinks", ctypes.c_void_p),
+                ("kv_quant", ctypes.POINTER(PaKvQuant))]
+
+
+PA_KV_INT8, PA_KV_FP8_E4M3 = 1, 2
+_KV_KIND = {"int8": PA_KV_INT8, "fp8": PA_KV_FP8_E4M3}
+CODE_DTYPES = (torch.int8, torch.uint8, torch.float8_e4m3fn)
+
+
+class KvQuant:
+    """A quantized cache's side data: ``kind`` "int8" or "fp8" (E4M3), the K
+    and V scale pools (float32 ``[P, ps, Hkv]`` views, any strides, the same
+    for both) and optional key smoothing factors (float32 ``[Hkv, D]``)."""
+
+    def __init__(self, kind: str, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                 k_smooth: Optional[torch.Tensor] = None):
+        if kind not in _KV_KIND:
+            raise ValueError(f"kind must be int8 or fp8, not {kind!r}")
+        if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or k_scale.dim() != 3:
+            raise TypeError("scale pools must be float32 [P, ps, Hkv]")
+        if k_scale.shape != v_scale.shape or k_scale.stride() != v_scale.stride():
+            raise ValueError("k_scale and v_scale must have the same shape and strides")
+        if k_smooth is not None:
+            if k_smooth.dtype != torch.float32 or k_smooth.dim() != 2:
+                raise TypeError("k_smooth must be float32 [Hkv, D]")
+            k_smooth = k_smooth.contiguous()
+        self.kind, self.k_scale, self.v_scale, self.k_smooth = kind, k_scale, v_scale, k_smooth
+
+    def struct(self) -> PaKvQuant:
+        q = PaKvQuant()
+        q.kv_dtype = _KV_KIND[self.kind]
+        q.k_scale, q.v_scale = self.k_scale.data_ptr(), self.v_scale.data_ptr()
+        q.scale_stride_page, q.scale_stride_slot, q.scale_stride_head = self.k_scale.stride()
+        q.k_smooth = self.k_smooth.data_ptr() if self.k_smooth is not None else None
+        return q
+
+
+def empty_code_pool(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int, kind: str = "int8",
+                    device="cuda", layout: str = "head_major") -> torch.Tensor:
+    """A 1-byte code pool (int8, or float8_e4m3fn for "fp8") as a ``[P, ps, Hkv, D]`` view."""
+    dt = torch.int8 if kind == "int8" else torch.float8_e4m3fn
+    return empty_pool(num_pages, page_size, num_kv_heads, head_dim, dtype=dt, device=device, layout=layout)
+
+
+def empty_scale_pool(num_pages: int, page_size: int, num_kv_heads: int, device="cuda",
+                     layout: str = "head_major") -> torch.Tensor:
+    """A float32 scale pool as a ``[P, ps, Hkv]`` view (``[P, Hkv, ps]`` in memory for "head_major")."""
+    if layout == "head_major":
+        return torch.empty(num_pages, num_kv_heads, page_size, dtype=torch.float32, device=device).permute(0, 2, 1)
+    if layout == "interleaved":
+        return torch.empty(num_pages, page_size, num_kv_heads, dtype=torch.float32, device=device)
+    raise ValueError(f"unknown pool layout {layout!r}")
 
 
 class PagedAttnError(RuntimeError):
@@ -66,6 +124,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_opts.argtypes = [vp, vp, vp, i32p, i32p, i32p, ctypes.c_float, ctypes.c_int, vp, vp,
                                          ctypes.c_size_t, ctypes.POINTER(PaDims), ctypes.c_int,
                                          ctypes.POINTER(PaAttnOpts), vp]
+    lib.kv_cache_write_quant.restype = ctypes.c_int
+    lib.kv_cache_write_quant.argtypes = [vp, vp, vp, vp, i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.POINTER(PaDims), ctypes.c_int, ctypes.POINTER(PaKvQuant), vp]
     lib.kv_cache_write.restype = ctypes.c_int
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.POINTER(PaDims), ctypes.c_int, vp]
@@ -174,19 +235,24 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                     causal: bool = True, *, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, max_query_len: Optional[int] = None,
                     num_splits: int = 0, window: int = 0, sinks: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
+                    kv_quant: Optional[KvQuant] = None, stream=None) -> torch.Tensor:
     """Causal GQA attention of q over the paged pools; returns ``out`` [N, Hq, D].
 
     ``scale`` defaults to 1/sqrt(D).  ``max_query_len`` is a host bound on any
     sequence's query tokens (default N); ``num_splits`` 0 picks the split count.
     ``window`` > 0 is a sliding window (a row sees its last ``window``
     positions) and ``sinks`` a float32 [Hq] device tensor of sink logits; with
-    either set the call goes through ``paged_attention_opts``.
+    either set the call goes through ``paged_attention_opts``.  With
+    ``kv_quant`` the pools are 1-byte code pools (int8 / float8_e4m3fn) and
+    q must be bfloat16.
     """
     lib = load_library()
     if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
         raise ValueError("k_pool and v_pool must have the same shape and strides")
-    if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
+    if kv_quant is not None:
+        if k_pool.dtype not in CODE_DTYPES or v_pool.dtype not in CODE_DTYPES:
+            raise TypeError("quantized pools hold 1-byte codes (int8 or float8_e4m3fn)")
+    elif q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
         raise TypeError("q and the pools must share one dtype")
     if out is None:
         out = torch.empty_like(q)
@@ -202,12 +268,14 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    if window or sinks is not None:
+    if window or sinks is not None or kv_quant is not None:
         if sinks is not None:
             if sinks.dtype != torch.float32 or sinks.device != q.device or sinks.numel() != q.shape[1]:
                 raise ValueError("sinks must be a float32 tensor of num_q_heads values on q's device")
             sinks = sinks.contiguous()
-        opts = PaAttnOpts(int(window), 0, sinks.data_ptr() if sinks is not None else None)
+        kq = kv_quant.struct() if kv_quant is not None else None
+        opts = PaAttnOpts(int(window), 0, sinks.data_ptr() if sinks is not None else None,
+                          ctypes.pointer(kq) if kq is not None else None)
         st = lib.paged_attention_opts(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), bt.data_ptr(),
                                       cl.data_ptr(), qsl.data_ptr(), float(scale), 1 if causal else 0,
                                       out.data_ptr(), ws_ptr, ws_bytes, ctypes.byref(dims), code,
@@ -241,6 +309,30 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tenso
                             _dtype_code(k_new.dtype), _stream_ptr(stream))
     if st != PA_OK:
         raise PagedAttnError(st, "kv_cache_write")
+
+
+def kv_cache_write_quant(k_new: torch.Tensor, v_new: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                         slot_mapping: torch.Tensor, kv_quant: KvQuant, stream=None) -> None:
+    """Quantize k_new/v_new [T, Hkv, D] (bf16 or float32) into the code and
+    scale pools at slot_mapping[T] (-1 = skip)."""
+    lib = load_library()
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must have the same shape and strides")
+    if k_new.stride(2) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if k_codes.dtype not in CODE_DTYPES or k_codes.shape != v_codes.shape or k_codes.stride() != v_codes.stride():
+        raise TypeError("code pools must be matching 1-byte [P, ps, Hkv, D] tensors")
+    dims = PaDims()
+    P, ps, Hkv, D = k_codes.shape
+    dims.num_kv_heads, dims.head_dim, dims.page_size, dims.num_pages = int(Hkv), int(D), int(ps), int(P)
+    dims.kv_stride_page, dims.kv_stride_slot, dims.kv_stride_head = k_codes.stride(0), k_codes.stride(1), k_codes.stride(2)
+    sm = _i32(slot_mapping, "slot_mapping")
+    kq = kv_quant.struct()
+    st = lib.kv_cache_write_quant(k_new.data_ptr(), v_new.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+                                  sm.data_ptr(), int(k_new.shape[0]), k_new.stride(0), k_new.stride(1),
+                                  ctypes.byref(dims), _dtype_code(k_new.dtype), ctypes.byref(kq), _stream_ptr(stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "kv_cache_write_quant")
 
 
 def validate(block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor, *,

@@ -15,6 +15,7 @@ hipError_t launch_prefill(const AttnParams& p, hipStream_t st);
 hipError_t launch_f32(const AttnParams& p, int max_q, hipStream_t st);
 hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
+hipError_t launch_kv_write_quant(const KvWriteParams& p, hipStream_t st);
 
 static std::atomic<int> g_cu_cache[64];
 
@@ -32,6 +33,19 @@ static int cu_count() {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Argument checks of a quantized-pool description (nothing is read from the
+// device): a known code type, non-negative scale strides, 16-byte kv strides
+// (1-byte codes), 4-byte aligned scale and smoothing pointers.
+static pa_status check_kv_quant(const pa_kv_quant* q, const pa_dims* d) {
+  if (q->kv_dtype != PA_KV_INT8 && q->kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (q->reserved0 != 0) return PA_ERR_SHAPE;
+  if (q->scale_stride_page < 0 || q->scale_stride_slot < 0 || q->scale_stride_head < 0) return PA_ERR_SHAPE;
+  if (d->kv_stride_page % 16 || d->kv_stride_slot % 16 || d->kv_stride_head % 16) return PA_ERR_UNSUPPORTED;
+  if (!aligned4(q->k_scale) || !aligned4(q->v_scale) || !aligned4(q->k_smooth)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
 
 // Two side streams and their events per device, so the launches of a mixed
 // batch (prefill tiles, 16-row decode tiles, verification tiles) run side by
@@ -132,10 +146,17 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   const float* sinks = opts ? opts->sinks : nullptr;
   if (window < 0 || (opts && opts->reserved0 != 0)) return PA_ERR_SHAPE;
   if (sinks && ((uintptr_t)sinks & 3u)) return PA_ERR_UNSUPPORTED;
+  const pa_kv_quant* kq = opts ? opts->kv_quant : nullptr;
+  if (kq) {
+    if ((st = check_kv_quant(kq, dims)) != PA_OK) return st;
+    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  }
   if (dims->num_seqs == 0 || dims->num_tokens == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start_loc || !out) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_UNSUPPORTED;
+  if (kq && (!kq->k_scale || !kq->v_scale)) return PA_ERR_NULL;
   const Plan pl = make_plan(dims, dtype, cu_count(), window);
+  if (kq && pl.prefill) return PA_ERR_UNSUPPORTED;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
 
@@ -184,6 +205,15 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   p.comb_splits_big = pl.dec_big || dtype == PA_F32 ? pl.splits_big : 1;
   p.window = pl.window;
   p.sinks = sinks;
+  if (kq) {
+    p.kv_code = kq->kv_dtype == PA_KV_INT8 ? KV_INT8 : KV_FP8;
+    p.k_scale = kq->k_scale;
+    p.v_scale = kq->v_scale;
+    p.sc_stride_page = kq->scale_stride_page;
+    p.sc_stride_slot = kq->scale_stride_slot;
+    p.sc_stride_head = kq->scale_stride_head;
+    p.k_smooth = kq->k_smooth;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
@@ -274,6 +304,56 @@ pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, voi
   p.num_pages = dims->num_pages;
   p.elem_bytes = dtype == PA_BF16 ? 2 : 4;
   return launch_kv_write(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status kv_cache_write_quant(const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                               const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
+                               int64_t new_stride_head, const pa_dims* dims, pa_dtype new_dtype,
+                               const pa_kv_quant* quant, void* stream) {
+  if (!dims || !quant) return PA_ERR_NULL;
+  if (new_dtype != PA_F32 && new_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || new_stride_tok < 0 || new_stride_head < 0) return PA_ERR_SHAPE;
+  if (dims->num_kv_heads < 1 || dims->num_pages < 0) return PA_ERR_SHAPE;
+  if (dims->head_dim != 64 && dims->head_dim != 128 && dims->head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (dims->page_size != 16 && dims->page_size != 32 && dims->page_size != 64 && dims->page_size != 128)
+    return PA_ERR_UNSUPPORTED;
+  if (dims->kv_stride_page < 0 || dims->kv_stride_slot < 0 || dims->kv_stride_head < 0) return PA_ERR_SHAPE;
+  pa_status st = check_kv_quant(quant, dims);
+  if (st != PA_OK) return st;
+  if (dims->num_kv_heads > 1 && (new_stride_head < dims->head_dim || dims->kv_stride_head < dims->head_dim))
+    return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_codes || !v_codes || !slot_mapping || !quant->k_scale || !quant->v_scale)
+    return PA_ERR_NULL;
+  const int64_t vec = new_dtype == PA_BF16 ? 8 : 4;
+  if (new_stride_tok % vec || new_stride_head % vec) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_codes) || !aligned16(v_codes))
+    return PA_ERR_UNSUPPORTED;
+  KvWriteParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool = k_codes;
+  p.v_pool = v_codes;
+  p.slot_mapping = slot_mapping;
+  p.new_stride_tok = new_stride_tok;
+  p.new_stride_head = new_stride_head;
+  p.kv_stride_page = dims->kv_stride_page;
+  p.kv_stride_slot = dims->kv_stride_slot;
+  p.kv_stride_head = dims->kv_stride_head;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = dims->num_kv_heads;
+  p.head_dim = dims->head_dim;
+  p.page_size = dims->page_size;
+  p.num_pages = dims->num_pages;
+  p.elem_bytes = new_dtype == PA_BF16 ? 2 : 4;
+  p.kv_code = quant->kv_dtype == PA_KV_INT8 ? KV_INT8 : KV_FP8;
+  p.k_scale = quant->k_scale;
+  p.v_scale = quant->v_scale;
+  p.sc_stride_page = quant->scale_stride_page;
+  p.sc_stride_slot = quant->scale_stride_slot;
+  p.sc_stride_head = quant->scale_stride_head;
+  p.k_smooth = quant->k_smooth;
+  return launch_kv_write_quant(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,

@@ -242,4 +242,87 @@ hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Quantizing KV write (page "32. Production attention kernels", Quantized KV
+// caches: quantize on write, once per token, one scale per (token, KV head)).
+// One workgroup per token, one wave per (head, K or V) vector: each lane
+// holds D/64 elements in float32; keys are divided by their smoothing
+// factors; amax = max(max |x|, 1e-8) by a wave reduction (exact);
+// scale = amax / q_max; code = x / scale rounded half-to-even and clamped to
+// +-127 (int8) or converted to float8 E4M3 by the hardware's round-to-nearest-
+// even conversion.  Each step is one correctly rounded float32 operation.
+// ---------------------------------------------------------------------------
+template <int D, int KQ>
+__global__ __launch_bounds__(256) void kv_write_quant_kernel(const KvWriteParams p) {
+  constexpr int EPL = D / 64;                    // elements per lane
+  const int i = blockIdx.x;
+  const int slot = p.slot_mapping[i];
+  if (slot < 0 || slot >= p.num_pages * p.page_size) return;
+  const int page = slot / p.page_size, off = slot % p.page_size;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float q_max = KQ == KV_INT8 ? 127.f : 448.f;
+  for (int item = wave; item < 2 * p.num_kv_heads; item += 4) {
+    const int h = item >> 1;
+    const bool is_v = item & 1;
+    const int64_t src = (int64_t)i * p.new_stride_tok + (int64_t)h * p.new_stride_head + lane * EPL;
+    float x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if (p.elem_bytes == 2) x[e] = (float)((const __bf16*)(is_v ? p.v_new : p.k_new))[src + e];
+      else x[e] = ((const float*)(is_v ? p.v_new : p.k_new))[src + e];
+    }
+    if (!is_v && p.k_smooth) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = x[e] / p.k_smooth[(int64_t)h * D + lane * EPL + e];
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
+    a = wave_max(a);
+    const float scale = fmaxf(a, 1e-8f) / q_max;
+    uint8_t code[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float y = x[e] / scale;
+      if constexpr (KQ == KV_INT8) {
+        const float r = fminf(fmaxf(rintf(y), -127.f), 127.f);
+        code[e] = (uint8_t)(int8_t)(int)r;
+      } else {
+        code[e] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xff);
+      }
+    }
+    uint8_t* dst = (uint8_t*)(is_v ? p.v_pool : p.k_pool) + (int64_t)page * p.kv_stride_page +
+                   (int64_t)off * p.kv_stride_slot + (int64_t)h * p.kv_stride_head + lane * EPL;
+    if constexpr (EPL == 1) {
+      dst[0] = code[0];
+    } else if constexpr (EPL == 2) {
+      *(uint16_t*)dst = (uint16_t)(code[0] | (code[1] << 8));
+    } else {
+      *(uint32_t*)dst = (uint32_t)code[0] | ((uint32_t)code[1] << 8) | ((uint32_t)code[2] << 16) |
+                        ((uint32_t)code[3] << 24);
+    }
+    if (lane == 0)
+      (is_v ? p.v_scale : p.k_scale)[(int64_t)page * p.sc_stride_page + (int64_t)off * p.sc_stride_slot +
+                                     (int64_t)h * p.sc_stride_head] = scale;
+  }
+}
+
+template <int D>
+static hipError_t launch_kv_write_quant_t(const KvWriteParams& p, hipStream_t st) {
+  if (p.kv_code == KV_INT8)
+    hipLaunchKernelGGL((kv_write_quant_kernel<D, KV_INT8>), dim3(p.num_tokens), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((kv_write_quant_kernel<D, KV_FP8>), dim3(p.num_tokens), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write_quant(const KvWriteParams& p, hipStream_t st) {
+  switch (p.head_dim) {
+    case 64: return launch_kv_write_quant_t<64>(p, st);
+    case 128: return launch_kv_write_quant_t<128>(p, st);
+    case 256: return launch_kv_write_quant_t<256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace pa

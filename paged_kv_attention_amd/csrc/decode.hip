@@ -35,6 +35,14 @@
 // sinks (same page, Stretch exercises): split 0 folds the head's sink logit
 // into its merged state as one more score with no value row.
 //
+// Quantized pools (page "Attention kernels", INT8 cache; page "32.
+// Production attention kernels", Quantized KV caches): K and V hold 1-byte
+// int8 or float8 E4M3 codes with one float32 scale per (slot, KV head).  The
+// codes are converted to bf16 in registers (exactly), a key's scale
+// multiplies its scores, a value's scale its probability before the PV
+// product, and the query is multiplied by the keys' smoothing factors once.
+// A chunk's 64 scales go through a small LDS area of the wave.
+//
 // The four waves' states are merged in LDS in a fixed order.  With one split
 // the normalised output is written directly; otherwise the unnormalised
 // partial (acc, m, l) goes to the float32 workspace for the combine kernel,
@@ -42,46 +50,55 @@
 // and KV Cache", Split-KV decode).
 #include <limits.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
 
-template <int D>
+template <int D, int KQ = KV_BF16>
 struct DecodeCfg {
   static constexpr int KC = 32;                  // keys per chunk: two 16-key MFMA tiles
   static constexpr int DS = D / 32;              // 32-dim k-steps of QK^T
   static constexpr int DT = D / 16;              // 16-dim output tiles of PV
-  static constexpr int CPL = D / 8;              // 16-byte chunks per key row
+  static constexpr int EB = KQ == KV_BF16 ? 2 : 1;   // bytes per cached element
+  static constexpr int CPL = D * EB / 16;        // 16-byte chunks per key row
+  static constexpr int EPC = 16 / EB;            // elements per 16-byte chunk
   static constexpr int VLOADS = KC * CPL / 64;   // 16-byte V loads per lane per chunk
-  static constexpr int ROW_BYTES = D * 2 + 32;   // V staging row stride (32 B pad: no bank conflicts
-                                                 // between the 4 rows a transpose read touches)
-  static constexpr int WAVE_LDS = KC * ROW_BYTES;
+  static constexpr int ROW_BYTES = D * 2 + 32;   // bf16 V staging row stride (32 B pad: no bank
+                                                 // conflicts between the 4 rows a transpose read touches)
+  static constexpr int SC_BYTES = KQ == KV_BF16 ? 0 : 64 * 4;   // the chunk's K and V scales
+  static constexpr int WAVE_LDS = KC * ROW_BYTES + SC_BYTES;
   static constexpr int NBUF = 1;                 // register chunks per wave (see the main loop)
 };
 
-template <int D, int NT>
+template <int D, int NT, int KQ>
 struct DecodeLds {
   static constexpr int ROWS = 16 * NT;
   static constexpr int ORS = D + 4;              // merge buffer row stride in floats
-  static constexpr int STAGE = 4 * DecodeCfg<D>::WAVE_LDS;
+  static constexpr int STAGE = 4 * DecodeCfg<D, KQ>::WAVE_LDS;
   static constexpr int MERGE = (8 * ROWS + ROWS * ORS) * 4;
   static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
 };
 
-template <int D>
+template <int D, int KQ>
 struct DecodeChunk {
-  bf16x8 k[2][DecodeCfg<D>::DS];
-  u32x4 v[DecodeCfg<D>::VLOADS];
+  // K: 8 dims of one key per (tile, k-step): bf16x8, or 8 codes
+  using KReg = typename std::conditional<KQ == KV_BF16, bf16x8, u32x2>::type;
+  KReg k[2][DecodeCfg<D, KQ>::DS];
+  u32x4 v[DecodeCfg<D, KQ>::VLOADS];
+  float sc;                                      // quantized: scale of key lane%32, K (lane<32) or V
 };
 
-// WIN: the launch has a sliding window (p.window > 0); SINK: sink logits
-// (p.sinks != null).  The plain instantiation carries none of their code.
-template <int D, int NT, bool WIN, bool SINK>
+// WIN: the launch has a sliding window (p.window > 0); KQ: the pools' code
+// type (KvCode).  The plain instantiation carries none of their code.
+template <int D, int NT, bool WIN, int KQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void decode_splitkv_kernel(const AttnParams p) {
-  using C = DecodeCfg<D>;
+  using C = DecodeCfg<D, KQ>;
+  constexpr bool QUANT = KQ != KV_BF16;
   constexpr int ROWS = 16 * NT;
-  constexpr int ORS = DecodeLds<D, NT>::ORS;
-  __shared__ __attribute__((aligned(16))) char smem[DecodeLds<D, NT>::BYTES];
+  constexpr int ORS = DecodeLds<D, NT, KQ>::ORS;
+  __shared__ __attribute__((aligned(16))) char smem[DecodeLds<D, NT, KQ>::BYTES];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -122,6 +139,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const __bf16* qp = (const __bf16*)p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) qB[nt][s] = *(const bf16x8*)(qp + 32 * s + 8 * q4);
+      if (QUANT && p.k_smooth) {
+        // q times the keys' smoothing factors undoes the smoothing in the scores
+        const float* sm = p.k_smooth + (int64_t)g * D;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          const f32x4 a = *(const f32x4*)(sm + 32 * s + 8 * q4);
+          const f32x4 b = *(const f32x4*)(sm + 32 * s + 8 * q4 + 4);
+          const bf16x8 v = qB[nt][s];
+          qB[nt][s] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2((float)v[0] * a[0], (float)v[1] * a[1]),
+                                                       pack_bf16x2((float)v[2] * a[2], (float)v[3] * a[3]),
+                                                       pack_bf16x2((float)v[4] * b[0], (float)v[5] * b[1]),
+                                                       pack_bf16x2((float)v[6] * b[2], (float)v[7] * b[3])});
+        }
+      }
     } else {
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) qB[nt][s] = bf16x8{};
@@ -139,8 +170,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   }
 
   PA_LDS char* vl = (PA_LDS char*)smem + wave * C::WAVE_LDS;
-  const __bf16* kbase = (const __bf16*)p.k_pool + (int64_t)g * p.kv_stride_head;
-  const __bf16* vbase = (const __bf16*)p.v_pool + (int64_t)g * p.kv_stride_head;
+  PA_LDS float* scl = (PA_LDS float*)(vl + C::KC * C::ROW_BYTES);   // quantized: [K scales 32][V scales 32]
+  // element strides are byte strides times EB
+  const char* kbase = (const char*)p.k_pool + (int64_t)g * p.kv_stride_head * C::EB;
+  const char* vbase = (const char*)p.v_pool + (int64_t)g * p.kv_stride_head * C::EB;
 
   // Address of slot `sl` of the page holding 16-key tile starting at key `kt`
   // (tiles never straddle pages: ps is a multiple of 16).  A tile past the
@@ -153,48 +186,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     return (int64_t)pg * p.kv_stride_page + (int64_t)slot * p.kv_stride_slot;
   };
 
-  auto load = [&](int c, DecodeChunk<D>& ch) {
+  auto load = [&](int c, DecodeChunk<D, KQ>& ch) {
     const int k0 = k_begin + c * C::KC;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const __bf16* kp = kbase + tile_off(k0 + 16 * t, l16) + 8 * q4;
+      const char* kp = kbase + (tile_off(k0 + 16 * t, l16) + 8 * q4) * C::EB;
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const bf16x8*)(kp + 32 * s);
+      for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const typename DecodeChunk<D, KQ>::KReg*)(kp + 32 * s * C::EB);
     }
 #pragma unroll
     for (int i = 0; i < C::VLOADS; ++i) {
       const int idx = i * 64 + lane;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       const int t = (i * 64 / C::CPL) / 16;       // uniform per load
-      const __bf16* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) + 8 * cc;
+      const char* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) * C::EB + 16 * cc;
       ch.v[i] = *(const u32x4*)vp;
+    }
+    if constexpr (QUANT) {
+      // lane l: scale of key k0 + l % 32, of K for l < 32 and of V above;
+      // keys outside the split (or below every window) get 0, so a stale
+      // scale in an unused slot never meets a probability
+      const int kk = k0 + (lane & 31);
+      const int lp = kk / ps;                    // a key past the last page reads that page's
+      const int64_t so = (int64_t)page_of(p, b, min(lp, npages - 1)) * p.sc_stride_page +   // slot kk % ps
+                         (int64_t)(kk - lp * ps) * p.sc_stride_slot + (int64_t)g * p.sc_stride_head;
+      const float sv = (lane < 32 ? p.k_scale : p.v_scale)[so];
+      ch.sc = (kk < k_end && (!WIN || kk >= wlo)) ? sv : 0.f;
     }
   };
 
-  auto process = [&](int c, const DecodeChunk<D>& ch) {
+  auto process = [&](int c, const DecodeChunk<D, KQ>& ch) {
     const int k0 = k_begin + c * C::KC;
     const bool need_mask = k0 + C::KC > mask_lim || k0 < win_all;
-    // V chunk -> this wave's LDS tile; rows past the split's end or before
-    // every row's window are selected to zero
+    // V chunk -> this wave's LDS tile as bf16; rows past the split's end or
+    // before every row's window are selected to zero
 #pragma unroll
     for (int i = 0; i < C::VLOADS; ++i) {
       const int idx = i * 64 + lane;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       u32x4 v = ch.v[i];
       if (need_mask && (k0 + kl >= k_end || (WIN && k0 + kl < wlo))) v = u32x4{0u, 0u, 0u, 0u};
-      *(PA_LDS u32x4*)(vl + kl * C::ROW_BYTES + cc * 16) = v;
+      if constexpr (QUANT) {
+        const u32x2 a = codes4_to_bf16<KQ>(v[0]), b2 = codes4_to_bf16<KQ>(v[1]);
+        const u32x2 c2 = codes4_to_bf16<KQ>(v[2]), d = codes4_to_bf16<KQ>(v[3]);
+        PA_LDS char* row = vl + kl * C::ROW_BYTES + cc * 32;
+        *(PA_LDS u32x4*)row = u32x4{a.x, a.y, b2.x, b2.y};
+        *(PA_LDS u32x4*)(row + 16) = u32x4{c2.x, c2.y, d.x, d.y};
+      } else {
+        *(PA_LDS u32x4*)(vl + kl * C::ROW_BYTES + cc * 16) = v;
+      }
+    }
+    f32x4 ksc[2], vsc[2];                         // quantized: scales of keys 16t + 4*q4 + r
+    if constexpr (QUANT) {
+      scl[lane] = ch.sc;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        ksc[t] = *(const PA_LDS f32x4*)(scl + 16 * t + 4 * q4);
+        vsc[t] = *(const PA_LDS f32x4*)(scl + 32 + 16 * t + 4 * q4);
+      }
     }
     // S^T = K . Q^T
     f32x4 st[2][NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 kf[C::DS];
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        if constexpr (QUANT) {
+          const u32x2 a = codes4_to_bf16<KQ>(ch.k[t][s].x), b2 = codes4_to_bf16<KQ>(ch.k[t][s].y);
+          kf[s] = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b2.x, b2.y});
+        } else {
+          kf[s] = ch.k[t][s];
+        }
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) a = mfma16(ch.k[t][s], qB[nt][s], a);
+        for (int s = 0; s < C::DS; ++s) a = mfma16(kf[s], qB[nt][s], a);
         st[t][nt] = a;
       }
+    }
     bf16x8 pB[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -204,7 +276,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = st[t][nt][r] * p.scale_log2;
+          float v = st[t][nt][r] * (QUANT ? p.scale_log2 * ksc[t][r] : p.scale_log2);
           if (need_mask) {
             const int j = k0 + 16 * t + 4 * q4 + r;
             const bool vis = j < k_end && (!causal || j <= diag + tok) && (!WIN || j > diag + tok - window);
@@ -221,14 +293,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const float alpha = fast_exp2(m_run[nt] - m_safe);
       m_run[nt] = m_new;
       uint32_t pk[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        pk[2 * t] = pack_bf16x2(fast_exp2(x[t][0] - m_safe), fast_exp2(x[t][1] - m_safe));
-        pk[2 * t + 1] = pack_bf16x2(fast_exp2(x[t][2] - m_safe), fast_exp2(x[t][3] - m_safe));
-      }
       float psum = 0.f;
+      if constexpr (QUANT) {
+        // l sums p; the PV operand is p times the value's scale
 #pragma unroll
-      for (int i = 0; i < 4; ++i) psum += bf16_lo(pk[i]) + bf16_hi(pk[i]);
+        for (int t = 0; t < 2; ++t) {
+          float e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[r] = fast_exp2(x[t][r] - m_safe);
+            psum += e[r];
+          }
+          pk[2 * t] = pack_bf16x2(e[0] * vsc[t][0], e[1] * vsc[t][1]);
+          pk[2 * t + 1] = pack_bf16x2(e[2] * vsc[t][2], e[3] * vsc[t][3]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          pk[2 * t] = pack_bf16x2(fast_exp2(x[t][0] - m_safe), fast_exp2(x[t][1] - m_safe));
+          pk[2 * t + 1] = pack_bf16x2(fast_exp2(x[t][2] - m_safe), fast_exp2(x[t][3] - m_safe));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) psum += bf16_lo(pk[i]) + bf16_hi(pk[i]);
+      }
       l_run[nt] = alpha * l_run[nt] + psum;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] *= alpha;
@@ -253,7 +340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   // the measured best on the 64 x 4096 decode step: a second chunk in flight
   // per wave (register double buffering, or issuing the next chunk's loads
   // before this chunk's softmax) lowers the achieved HBM bandwidth.
-  DecodeChunk<D> buf[C::NBUF];
+  DecodeChunk<D, KQ> buf[C::NBUF];
 #pragma unroll
   for (int j = 0; j < C::NBUF - 1; ++j)
     if (wave + 4 * j < nchunks) load(wave + 4 * j, buf[j]);
@@ -315,7 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
     float Lt = ((Lw[row] + Lw[ROWS + row]) + Lw[2 * ROWS + row]) + Lw[3 * ROWS + row];
     f32x4 o = *(const f32x4*)(Ob + row * ORS + 4 * c4);
-    if (SINK && split == 0) {
+    if (p.sinks && split == 0) {
       // the sink joins split 0 as one more score with no value row
       const float s2 = p.sinks[head] * kLog2e;
       const float Mn = fmaxf(M, s2);
@@ -340,15 +427,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 template <int D, int NT>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
-  const bool win = p.window > 0, sink = p.sinks != nullptr;
-  if (win && sink)
-    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, true>), grid, dim3(256), 0, st, p);
-  else if (win)
-    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, false>), grid, dim3(256), 0, st, p);
-  else if (sink)
-    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, true>), grid, dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, false>), grid, dim3(256), 0, st, p);
+  const bool win = p.window > 0;
+  switch (p.kv_code) {
+    case KV_INT8:
+      if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_INT8>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_INT8>), grid, dim3(256), 0, st, p);
+      break;
+    case KV_FP8:
+      if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_FP8>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_FP8>), grid, dim3(256), 0, st, p);
+      break;
+    default:
+      if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16>), grid, dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

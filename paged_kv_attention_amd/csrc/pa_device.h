@@ -58,6 +58,36 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const PA_LDS char* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Quantized cache codes -> bf16, exactly (|int8| <= 127 and every float8
+// E4M3 value fit bf16's 8 significant bits).  Byte i of word w is code i.
+enum KvCode : int { KV_BF16 = 0, KV_INT8 = 1, KV_FP8 = 2 };
+
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float (&f)[4]) {
+  const uint32_t u = w ^ 0x80808080u;            // signed -> biased unsigned bytes
+  f[0] = (float)(u & 0xffu) - 128.f;
+  f[1] = (float)((u >> 8) & 0xffu) - 128.f;
+  f[2] = (float)((u >> 16) & 0xffu) - 128.f;
+  f[3] = (float)(u >> 24) - 128.f;
+}
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&f)[4]) {
+  // gfx950 converts OCP E4M3 (the float8_e4m3fn format) in hardware
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+}
+template <int KQ>
+__device__ __forceinline__ void codes4_to_f32(uint32_t w, float (&f)[4]) {
+  if constexpr (KQ == KV_INT8) i8x4_to_f32(w, f);
+  else fp8x4_to_f32(w, f);
+}
+// 4 codes -> 4 bf16 (two packed words)
+template <int KQ>
+__device__ __forceinline__ u32x2 codes4_to_bf16(uint32_t w) {
+  float f[4];
+  codes4_to_f32<KQ>(w, f);
+  return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+}
+
 // Cross-lane helpers over the 64-lane wave.
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   int lane = __lane_id();

@@ -42,6 +42,13 @@ struct AttnParams {
   int32_t comb_splits_big;    // combine: splits of rows with n*G > 16
   int32_t window;           // sliding window: key j visible to position pos only if j > pos - window (0 = none)
   const float* sinks;       // [Hq] sink logits in scaled-score units, or null
+  // quantized pools (kv_code != 0): 1-byte codes, one float32 scale per
+  // (page, slot, KV head) and optional per-channel key smoothing [Hkv, D]
+  int32_t kv_code;          // 0 = pools in the q dtype, 1 = int8, 2 = fp8 E4M3
+  const float* k_scale;
+  const float* v_scale;
+  int64_t sc_stride_page, sc_stride_slot, sc_stride_head;
+  const float* k_smooth;
 };
 
 // First page of the split ranges of a sequence with context L and n step
@@ -61,7 +68,13 @@ struct KvWriteParams {
   int64_t new_stride_tok, new_stride_head;
   int64_t kv_stride_page, kv_stride_slot, kv_stride_head;
   int32_t num_tokens, num_kv_heads, head_dim, page_size, num_pages;
-  int32_t elem_bytes;
+  int32_t elem_bytes;       // bytes per element of the new rows
+  // quantizing write (kv_code != 0): pools hold 1-byte codes
+  int32_t kv_code;
+  float* k_scale;
+  float* v_scale;
+  int64_t sc_stride_page, sc_stride_slot, sc_stride_head;
+  const float* k_smooth;
 };
 
 }  // namespace pa
