@@ -54,16 +54,20 @@ def _key_range(L, n, window):
 
 
 def algorithmic_bytes(context_lens, query_lens, num_q_heads, num_kv_heads, head_dim, page_size, elem_bytes,
-                      window=0):
+                      window=0, kv_code_bytes=None, scale_bytes=0):
     """Bytes the method must move: K and V of every visible position once per
     GQA group, q read and out written once, the page ids of the pages used,
     the lengths and query offsets.  (Page "32. Production attention kernels",
     What the reference backend costs: 2 x Hkv x D values per token per layer.)
-    With a sliding window only the positions some row can see count."""
+    With a sliding window only the positions some row can see count.  A
+    quantized cache stores ``kv_code_bytes`` per element plus ``scale_bytes``
+    per (position, KV head) vector (page "32. Production attention kernels",
+    Quantized KV caches: 4 extra bytes per 128-value head vector)."""
+    per_vec = head_dim * (elem_bytes if kv_code_bytes is None else kv_code_bytes) + scale_bytes
     kv = ids = 0
     for L, n in zip(context_lens, query_lens):
         lo, hi = _key_range(L, n, window)
-        kv += (hi - lo) * num_kv_heads * head_dim * 2 * elem_bytes
+        kv += (hi - lo) * num_kv_heads * 2 * per_vec
         ids += ((hi + page_size - 1) // page_size - lo // page_size) * 4 if hi > lo else 0
     n = sum(query_lens)
     qo = n * num_q_heads * head_dim * elem_bytes * 2
@@ -198,7 +202,7 @@ class PrefillBench:
 class WorkloadBench:
     """Any seeded workload on device, pools rotated over `layers` sets."""
 
-    def __init__(self, config, layers=1, window=0, sinks=False):
+    def __init__(self, config, layers=1, window=0, sinks=False, kv_kind=None):
         import torch
         import paged_kv_attention_amd as pa
         from workloads import make
@@ -222,6 +226,21 @@ class WorkloadBench:
             k.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
             v.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
             self.pools.append((k, v))
+        self.kv_kind = kv_kind
+        self.quant = [None] * len(self.pools)
+        if kv_kind is not None:
+            # quantize every pool set on the device with the library's own write
+            qpools = []
+            slots = torch.arange(P * ps, dtype=torch.int32, device=dev)
+            for i, (k, v) in enumerate(self.pools):
+                kc = pa.empty_code_pool(P, ps, Hkv, D, kv_kind, dev)
+                vc = pa.empty_code_pool(P, ps, Hkv, D, kv_kind, dev)
+                kq = pa.KvQuant(kv_kind, pa.empty_scale_pool(P, ps, Hkv, dev), pa.empty_scale_pool(P, ps, Hkv, dev))
+                pa.kv_cache_write_quant(k.reshape(P * ps, Hkv, D), v.reshape(P * ps, Hkv, D), kc, vc, slots, kq)
+                qpools.append((kc, vc))
+                self.quant[i] = kq
+            torch.cuda.synchronize()
+            self.pools = qpools
         self.out = torch.empty_like(self.q)
         dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=w.max_query_len)
         self.ws = torch.empty(max(pa.workspace_size(dims, w.dtype), 16), dtype=torch.uint8, device=dev)
@@ -229,7 +248,8 @@ class WorkloadBench:
         lens = w.context_lens.tolist()
         e = 4 if w.dtype == torch.float32 else 2
         self.bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, ps, e,
-                                       window=window)
+                                       window=window, kv_code_bytes=None if kv_kind is None else 1,
+                                       scale_bytes=0 if kv_kind is None else 4)
         self.flops = algorithmic_flops(lens, w.query_lens, w.num_q_heads, w.head_dim, causal=w.causal,
                                        window=window)
         self.sinks = None if self.sinks_cpu is None else self.sinks_cpu.to(dev)
@@ -239,7 +259,7 @@ class WorkloadBench:
         w = self.w
         return self.pa.paged_attention(self.q, k, v, self.bt, self.cl, self.qsl, w.scale, w.causal, out=self.out,
                                        workspace=self.ws, max_query_len=w.max_query_len, window=self.window,
-                                       sinks=self.sinks)
+                                       sinks=self.sinks, kv_quant=self.quant[layer % len(self.pools)])
 
 
 
@@ -267,22 +287,31 @@ def other_workloads(steps, warmup):
 
 
 def variant_workloads(steps, warmup):
-    """The sliding-window and attention-sink variants at the headline shapes:
-    the 64 x 4096 decode with a 1024-position window (HBM-bound: only the
-    window's K/V count) and the 4 x 8192 causal prefill with a 4096-position
-    window (MFMA-bound: only the band's pairs count), both with one sink
-    logit per query head."""
+    """The variants at the headline shapes: the 64 x 4096 decode with a
+    1024-position window (HBM-bound: only the window's K/V count) and the
+    4 x 8192 causal prefill with a 4096-position window (MFMA-bound: only the
+    band's pairs count), both with one sink logit per query head; and the
+    decode over int8 and fp8 caches (bytes: 1-byte codes plus a float32
+    scale per position and KV head), and the prefill over an int8 cache."""
     import torch
     res = {}
-    for cfg, layers, window, bound, name in [
-            (3, 4, 1024, "hbm", "bf16 decode 64 x 4096, 32/8 heads, D 128, page 64, window 1024, sinks"),
-            (5, 1, 4096, "mfma", "bf16 causal prefill 4 x 8192, 32/8 heads, D 128, page 64, window 4096, sinks")]:
+    for cfg, layers, window, sinks, kind, bound, key, name in [
+            (3, 4, 1024, True, None, "hbm", "config3_window1024_sinks",
+             "bf16 decode 64 x 4096, 32/8 heads, D 128, page 64, window 1024, sinks"),
+            (5, 1, 4096, True, None, "mfma", "config5_window4096_sinks",
+             "bf16 causal prefill 4 x 8192, 32/8 heads, D 128, page 64, window 4096, sinks"),
+            (3, 4, 0, False, "int8", "hbm", "config3_int8_kv",
+             "decode 64 x 4096, 32/8 heads, D 128, page 64, bf16 q over an int8 KV cache (scale per token and head)"),
+            (3, 4, 0, False, "fp8", "hbm", "config3_fp8_kv",
+             "decode 64 x 4096, 32/8 heads, D 128, page 64, bf16 q over an fp8 E4M3 KV cache (scale per token and head)"),
+            (5, 1, 0, False, "int8", "mfma", "config5_int8_kv",
+             "causal prefill 4 x 8192, 32/8 heads, D 128, page 64, bf16 q over an int8 KV cache")]:
         print(f"[bench] variant: {name}", file=sys.stderr, flush=True)
-        wb = WorkloadBench(cfg, layers, window=window, sinks=True)
+        wb = WorkloadBench(cfg, layers, window=window, sinks=sinks, kv_kind=kind)
         vsteps = steps if bound == "hbm" else max(3, min(steps, 10))
         _, per = _time_steps([wb.attend], vsteps, warmup)
         ms = per[0]
-        entry = {"workload": name, "ms": round(ms, 5), "window": window, "splits": wb.splits,
+        entry = {"workload": name, "ms": round(ms, 5), "window": window, "kv_cache": kind or "bf16", "splits": wb.splits,
                  "algorithmic_bytes": wb.bytes, "algorithmic_flops": wb.flops, "pool_sets_rotated": layers}
         if bound == "hbm":
             gbs = wb.bytes / (ms * 1e-3) / 1e9
@@ -294,7 +323,7 @@ def variant_workloads(steps, warmup):
             entry.update({"TFLOP_s": round(tf, 2), "roofline": {"bound": "mfma", "achieved": round(tf, 2),
                                                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                                                 "frac": round(tf / BF16_PEAK_TFLOPS, 4)}})
-        res[f"config{cfg}_window{window}_sinks"] = entry
+        res[key] = entry
         del wb
         torch.cuda.empty_cache()
     return res

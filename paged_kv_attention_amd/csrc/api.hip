@@ -156,7 +156,6 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_UNSUPPORTED;
   if (kq && (!kq->k_scale || !kq->v_scale)) return PA_ERR_NULL;
   const Plan pl = make_plan(dims, dtype, cu_count(), window);
-  if (kq && pl.prefill) return PA_ERR_UNSUPPORTED;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
 

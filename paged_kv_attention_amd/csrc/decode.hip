@@ -69,7 +69,7 @@ struct DecodeCfg {
                                                  // conflicts between the 4 rows a transpose read touches)
   static constexpr int SC_BYTES = KQ == KV_BF16 ? 0 : 64 * 4;   // the chunk's K and V scales
   static constexpr int WAVE_LDS = KC * ROW_BYTES + SC_BYTES;
-  static constexpr int NBUF = 1;                 // register chunks per wave (see the main loop)
+  static constexpr int NBUF = KQ == KV_BF16 ? 1 : 2;   // register chunks per wave (see the main loop)
 };
 
 template <int D, int NT, int KQ>
@@ -159,6 +159,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     }
   }
 
+  // int8 pools enter the MFMAs as c + 128 (one conversion per code); the
+  // scores then lose 128 * sum_d q_d and the outputs 128 * sum_j p'_j, with
+  // qsum the row sum of the bf16 query and pvsum the row sum of the
+  // probabilities the PV product used (rescaled with the accumulator).
+  constexpr bool BIAS = KQ == KV_INT8;
+  float qsum[NT], pvsum[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float a = 0.f;
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += (float)qB[nt][s][e];
+      a += shfl_xor(a, 16);
+      a += shfl_xor(a, 32);
+    }
+    qsum[nt] = a;
+    pvsum[nt] = 0.f;
+  }
+
   f32x4 acc[NT][C::DT];
   float m_run[NT], l_run[NT];
 #pragma unroll
@@ -226,7 +247,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       u32x4 v = ch.v[i];
       if (need_mask && (k0 + kl >= k_end || (WIN && k0 + kl < wlo))) v = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (QUANT) {
+      if constexpr (BIAS) {
+        const u32x2 a = i8x4_to_bf16_biased(v[0]), b2 = i8x4_to_bf16_biased(v[1]);
+        const u32x2 c2 = i8x4_to_bf16_biased(v[2]), d = i8x4_to_bf16_biased(v[3]);
+        PA_LDS char* row = vl + kl * C::ROW_BYTES + cc * 32;
+        *(PA_LDS u32x4*)row = u32x4{a.x, a.y, b2.x, b2.y};
+        *(PA_LDS u32x4*)(row + 16) = u32x4{c2.x, c2.y, d.x, d.y};
+      } else if constexpr (QUANT) {
         const u32x2 a = codes4_to_bf16<KQ>(v[0]), b2 = codes4_to_bf16<KQ>(v[1]);
         const u32x2 c2 = codes4_to_bf16<KQ>(v[2]), d = codes4_to_bf16<KQ>(v[3]);
         PA_LDS char* row = vl + kl * C::ROW_BYTES + cc * 32;
@@ -252,7 +279,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       bf16x8 kf[C::DS];
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) {
-        if constexpr (QUANT) {
+        if constexpr (BIAS) {
+          const u32x2 a = i8x4_to_bf16_biased(ch.k[t][s].x), b2 = i8x4_to_bf16_biased(ch.k[t][s].y);
+          kf[s] = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b2.x, b2.y});
+        } else if constexpr (QUANT) {
           const u32x2 a = codes4_to_bf16<KQ>(ch.k[t][s].x), b2 = codes4_to_bf16<KQ>(ch.k[t][s].y);
           kf[s] = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b2.x, b2.y});
         } else {
@@ -276,7 +306,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = st[t][nt][r] * (QUANT ? p.scale_log2 * ksc[t][r] : p.scale_log2);
+          float v = (BIAS ? st[t][nt][r] - 128.f * qsum[nt] : st[t][nt][r]) *
+                    (QUANT ? p.scale_log2 * ksc[t][r] : p.scale_log2);
           if (need_mask) {
             const int j = k0 + 16 * t + 4 * q4 + r;
             const bool vis = j < k_end && (!causal || j <= diag + tok) && (!WIN || j > diag + tok - window);
@@ -306,6 +337,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
           }
           pk[2 * t] = pack_bf16x2(e[0] * vsc[t][0], e[1] * vsc[t][1]);
           pk[2 * t + 1] = pack_bf16x2(e[2] * vsc[t][2], e[3] * vsc[t][3]);
+        }
+        if constexpr (BIAS) {
+          float ps_ = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ps_ += bf16_lo(pk[i]) + bf16_hi(pk[i]);
+          pvsum[nt] = alpha * pvsum[nt] + ps_;
         }
       } else {
 #pragma unroll
@@ -359,6 +396,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   for (int nt = 0; nt < NT; ++nt) {
     l_run[nt] += shfl_xor(l_run[nt], 16);
     l_run[nt] += shfl_xor(l_run[nt], 32);
+    if constexpr (BIAS) {
+      // remove the +128 of the int8 value codes: sum_j p'_j (c_j + 128) - 128 sum_j p'_j
+      float s_ = pvsum[nt];
+      s_ += shfl_xor(s_, 16);
+      s_ += shfl_xor(s_, 32);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] -= 128.f * s_;
+    }
   }
   __syncthreads();                              // staging tiles are free from here on
   float* Mw = (float*)smem;                     // [4][ROWS]

@@ -80,6 +80,14 @@ __device__ __forceinline__ void codes4_to_f32(uint32_t w, float (&f)[4]) {
   if constexpr (KQ == KV_INT8) i8x4_to_f32(w, f);
   else fp8x4_to_f32(w, f);
 }
+// 4 int8 codes c -> 4 bf16 holding c + 128 (0..255, exact): one conversion
+// per value; the kernels subtract 128 times the operand sum afterwards.
+__device__ __forceinline__ u32x2 i8x4_to_bf16_biased(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  return u32x2{pack_bf16x2((float)(u & 0xffu), (float)((u >> 8) & 0xffu)),
+               pack_bf16x2((float)((u >> 16) & 0xffu), (float)(u >> 24))};
+}
+
 // 4 codes -> 4 bf16 (two packed words)
 template <int KQ>
 __device__ __forceinline__ u32x2 codes4_to_bf16(uint32_t w) {

@@ -35,11 +35,18 @@
 // sink (same page, Stretch exercises) is folded into each row's state before
 // the normalisation, as one more score with no value row.
 //
+// Quantized pools (page "Attention kernels", INT8 cache): a block's 1-byte
+// codes are loaded (half the bytes), multiplied by their key's scale and
+// rounded to bf16 when the block is staged in LDS, so the loop itself is the
+// bf16 one; the query is multiplied by the keys' smoothing factors once.
+//
 // Tiles with more keys run first (page "Attention kernels", Open questions:
 // heaviest causal blocks first), and the flat block index is remapped so
 // that the tiles of one (sequence, KV head) land on the same XCD and share
 // its L2.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 
@@ -65,14 +72,20 @@ struct PrefillCfg {
   static constexpr float TAU = 8.f;              // lazy-rescale threshold (log2 units)
 };
 
-template <int D, int NW, int KB>
+// A thread's share of one K/V block in registers: 16-byte bf16 chunks, or
+// for quantized pools the same 8 elements as 8-byte codes plus their key's
+// K and V scales.
+template <int D, int NW, int KB, int KQ = KV_BF16>
 struct PrefillRegs {
-  u32x4 k[PrefillCfg<D, NW, 1, KB>::LOADS], v[PrefillCfg<D, NW, 1, KB>::LOADS];
+  static constexpr int N = PrefillCfg<D, NW, 1, KB>::LOADS;
+  using Chunk = typename std::conditional<KQ == KV_BF16, u32x4, u32x2>::type;
+  Chunk k[N], v[N];
+  float ks[KQ == KV_BF16 ? 1 : N], vs[KQ == KV_BF16 ? 1 : N];
 };
 
-// WIN: the launch has a sliding window (p.window > 0); the windowless
-// instantiation carries none of its bounds or masks.
-template <int D, int NW, int PF, int KB, bool WIN>
+// WIN: the launch has a sliding window (p.window > 0); KQ: the pools' code
+// type (KvCode).  The plain instantiation carries none of their code.
+template <int D, int NW, int PF, int KB, bool WIN, int KQ>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void prefill_kernel(const AttnParams p) {
   using C = PrefillCfg<D, NW, PF, KB>;
@@ -136,6 +149,20 @@ void prefill_kernel(const AttnParams p) {
       w ^= u32x4{qsign, qsign, qsign, qsign};
       qB[s] = __builtin_bit_cast(bf16x8, w);
     }
+    if (KQ != KV_BF16 && p.k_smooth) {
+      // q times the keys' smoothing factors undoes the smoothing in the scores
+      const float* sm = p.k_smooth + (int64_t)g * D + 8 * h2;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        const f32x4 a = *(const f32x4*)(sm + 16 * s);
+        const f32x4 c2 = *(const f32x4*)(sm + 16 * s + 4);
+        const bf16x8 v = qB[s];
+        qB[s] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2((float)v[0] * a[0], (float)v[1] * a[1]),
+                                                 pack_bf16x2((float)v[2] * a[2], (float)v[3] * a[3]),
+                                                 pack_bf16x2((float)v[4] * c2[0], (float)v[5] * c2[1]),
+                                                 pack_bf16x2((float)v[6] * c2[2], (float)v[7] * c2[3])});
+      }
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) qB[s] = bf16x8{};
@@ -155,35 +182,83 @@ void prefill_kernel(const AttnParams p) {
   // The 64 threads of a wave cover 64/CPL consecutive keys of one page, so
   // the page id is wave-uniform: it comes from a scalar load (counted by
   // lgkmcnt), and waiting for it never waits for the K/V loads in flight.
-  auto gload = [&](int blk, PrefillRegs<D, NW, KB>& r) {
+  auto gload = [&](int blk, PrefillRegs<D, NW, KB, KQ>& r) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NTH + threadIdx.x;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       const int jw = __builtin_amdgcn_readfirstlane(blk * C::KB + (i * C::NTH + (threadIdx.x & ~63)) / C::CPL);
       const int j = blk * C::KB + kl;
-      r.k[i] = u32x4{0u, 0u, 0u, 0u};
-      r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (KQ == KV_BF16) {
+        r.k[i] = u32x4{0u, 0u, 0u, 0u};
+        r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        r.k[i] = u32x2{0u, 0u};
+        r.v[i] = u32x2{0u, 0u};
+        r.ks[i] = 0.f;                           // keys outside the range dequantize to 0, whatever
+        r.vs[i] = 0.f;                           // an unused slot's scale holds
+      }
       if (jw < L) {
         const int lp = jw >> psh;
-        const int64_t pbase = (int64_t)page_of(p, b, lp) * p.kv_stride_page;
+        const int pg = page_of(p, b, lp);
+        const int64_t pbase = (int64_t)pg * p.kv_stride_page;
         if (j < L && (!WIN || j >= wlo_tile)) {
-          const int64_t off = pbase + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;
-          r.k[i] = *(const u32x4*)(kbase + off);
-          r.v[i] = *(const u32x4*)(vbase + off);
+          const int64_t off = pbase + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;   // elements
+          if constexpr (KQ == KV_BF16) {
+            r.k[i] = *(const u32x4*)(kbase + off);
+            r.v[i] = *(const u32x4*)(vbase + off);
+          } else {
+            r.k[i] = *(const u32x2*)((const char*)p.k_pool + (int64_t)g * p.kv_stride_head + off);
+            r.v[i] = *(const u32x2*)((const char*)p.v_pool + (int64_t)g * p.kv_stride_head + off);
+            const int64_t so = (int64_t)pg * p.sc_stride_page + (int64_t)(j - (lp << psh)) * p.sc_stride_slot +
+                               (int64_t)g * p.sc_stride_head;
+            r.ks[i] = p.k_scale[so];
+            r.vs[i] = p.v_scale[so];
+          }
         }
       }
     }
   };
-  auto lstore = [&](int buf, const PrefillRegs<D, NW, KB>& r) {
+  // quantized: 8 codes times their key's scale, rounded to bf16.  An int8
+  // code c is converted as c + 128 and fma(c + 128, s, -128 s) = c s exactly
+  // before the one rounding, so both forms give the same bits.
+  auto dequant8 = [&](u32x2 w, float sc) -> u32x4 {
+    float f[8];
+    if constexpr (KQ == KV_INT8) {
+      const float off = -128.f * sc;
+      const uint32_t u0 = w.x ^ 0x80808080u, u1 = w.y ^ 0x80808080u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = fmaf((float)((u0 >> (8 * e)) & 0xffu), sc, off);
+        f[4 + e] = fmaf((float)((u1 >> (8 * e)) & 0xffu), sc, off);
+      }
+    } else {
+      float a[4], h[4];
+      codes4_to_f32<KQ == KV_BF16 ? KV_FP8 : KQ>(w.x, a);
+      codes4_to_f32<KQ == KV_BF16 ? KV_FP8 : KQ>(w.y, h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = a[e] * sc;
+        f[4 + e] = h[e] * sc;
+      }
+    }
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
+  };
+  auto lstore = [&](int buf, const PrefillRegs<D, NW, KB, KQ>& r) {
     PA_LDS char* kl_ = lds + buf * C::STAGE;
     PA_LDS char* vl_ = kl_ + C::KBYTES;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NTH + threadIdx.x;
       const int kl = idx / C::CPL, cc = idx % C::CPL;
-      *(PA_LDS u32x4*)(kl_ + kl * C::KRS + cc * 16) = r.k[i];
-      *(PA_LDS u32x4*)(vl_ + kl * C::VRS + cc * 16) = r.v[i];
+      if constexpr (KQ == KV_BF16) {
+        *(PA_LDS u32x4*)(kl_ + kl * C::KRS + cc * 16) = r.k[i];
+        *(PA_LDS u32x4*)(vl_ + kl * C::VRS + cc * 16) = r.v[i];
+      } else {
+        *(PA_LDS u32x4*)(kl_ + kl * C::KRS + cc * 16) = dequant8(r.k[i], r.ks[i]);
+        *(PA_LDS u32x4*)(vl_ + kl * C::VRS + cc * 16) = dequant8(r.v[i], r.vs[i]);
+      }
     }
   };
 
@@ -299,7 +374,7 @@ void prefill_kernel(const AttnParams p) {
   // registers hold blocks blk+1 .. blk+PF, issued PF blocks ahead.
   f32x16 st[C::KT];
   uint32_t pk[C::KT][8];
-  PrefillRegs<D, NW, KB> rg[PF];
+  PrefillRegs<D, NW, KB, KQ> rg[PF];
   if (blk0 < nblk) {
     gload(blk0, rg[0]);
     lstore(blk0 & 1, rg[0]);
@@ -364,10 +439,21 @@ template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
   constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF, KB = PrefillShape<D>::KB;
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs;
-  if (p.window > 0)
-    hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false>), dim3((unsigned)total), dim3(64 * NW), 0, st, p);
+  const dim3 grid((unsigned)total), block(64 * NW);
+  const bool win = p.window > 0;
+  switch (p.kv_code) {
+    case KV_INT8:
+      if (win) hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true, KV_INT8>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_INT8>), grid, block, 0, st, p);
+      break;
+    case KV_FP8:
+      if (win) hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true, KV_FP8>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_FP8>), grid, block, 0, st, p);
+      break;
+    default:
+      if (win) hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true, KV_BF16>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 

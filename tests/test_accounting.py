@@ -59,3 +59,13 @@ def test_window_bytes_and_flops_closed_forms():
     assert bench.algorithmic_flops([10], [3], 1, 1, window=2) == 4 * 6
     # not causal: row at pos sees [pos - 1, 10), i.e. 4, 3 and 2 keys
     assert bench.algorithmic_flops([10], [3], 1, 1, causal=False, window=2) == 4 * (4 + 3 + 2)
+
+
+def test_quantized_cache_bytes_match_printed_int8_figure():
+    # one token of context, 8 KV heads x 128 dims, 1-byte codes plus a float32 scale per head vector
+    per_layer = bench.algorithmic_bytes([1], [0], 32, 8, 128, 64, 2, kv_code_bytes=1, scale_bytes=4) - 4 - 12
+    assert per_layer * 36 == GOLD["qwen3_8b_int8_bytes_per_token_36_layers"]["value"]
+    assert int(1e9 // (per_layer * 36)) == GOLD["qwen3_8b_int8_tokens_per_GB"]["value"]
+    # the 64 x 4096 decode over an int8 cache moves 132/256 of the bf16 K/V bytes
+    b8 = bench.algorithmic_bytes([4096] * 64, [1] * 64, 32, 8, 128, 64, 2, kv_code_bytes=1, scale_bytes=4)
+    assert b8 == 64 * 4096 * 8 * 2 * 132 + 64 * 32 * 128 * 2 * 2 + 64 * 64 * 4 + 129 * 4

@@ -173,15 +173,37 @@ def test_decode_64x4096_quantized_full(kind):
     _check(got, _ref(w, kc, vc, ks, vs), label=f"64x4096 {kind}")
 
 
-def test_quantized_prefill_is_refused_until_supported_or_matches():
-    """A prefill-class batch over a quantized cache either runs correctly or is refused with a status."""
-    w = make_custom(seed=640, context_lens=[300], query_lens=[100], num_q_heads=8, num_kv_heads=2, head_dim=128,
-                    page_size=64, dtype=torch.bfloat16)
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+@pytest.mark.parametrize("D,ps,layout,smooth", [(128, 64, "head_major", False), (64, 16, "interleaved", True),
+                                                (256, 32, "head_major", True)])
+def test_prefill_quantized(kind, D, ps, layout, smooth):
+    Hq, Hkv = (16, 4) if D == 256 else (8, 2)
+    w = make_custom(seed=640 + D, context_lens=[700, 1300, 90], query_lens=[700, 300, 90], num_q_heads=Hq,
+                    num_kv_heads=Hkv, head_dim=D, page_size=ps, dtype=torch.bfloat16)
+    sm = _smooth(Hkv, D, 9) if smooth else None
+    kc, vc, ks, vs = _quantized_cache(w, kind, sm)
+    kd, vd, kq = _to_dev_cache(kc, vc, ks, vs, kind, sm, layout)
+    got = _run(w, kd, vd, kq)
+    _check(got, _ref(w, kc, vc, ks, vs, sm), label=f"{kind} prefill D {D} ps {ps} smooth {smooth}")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_mixed_batch_quantized_window_sinks(kind):
+    w = make_custom(seed=650, context_lens=[1536, 900, 2048, 33, 700], query_lens=[512, 1, 5, 1, 40],
+                    num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, dtype=torch.bfloat16)
+    sm = _smooth(8, 128, 11)
+    kc, vc, ks, vs = _quantized_cache(w, kind, sm)
+    kd, vd, kq = _to_dev_cache(kc, vc, ks, vs, kind, sm)
+    sk = torch.randn(32, generator=torch.Generator().manual_seed(2)) * 2
+    got = _run(w, kd, vd, kq, window=300, sinks=sk.to(DEV))
+    _check(got, _ref(w, kc, vc, ks, vs, sm, window=300, sinks=sk.double()), label=f"{kind} mixed window sinks")
+
+
+def test_prefill_4x8192_int8_sampled():
+    """The 4 x 8192 causal prefill over an int8 cache, sampled rows."""
+    w = make(5)
     kc, vc, ks, vs = _quantized_cache(w, "int8")
     kd, vd, kq = _to_dev_cache(kc, vc, ks, vs, "int8")
-    try:
-        got = _run(w, kd, vd, kq)
-    except pa.PagedAttnError as e:
-        assert e.status == pa.PA_ERR_UNSUPPORTED
-        return
-    _check(got, _ref(w, kc, vc, ks, vs), label="int8 prefill")
+    got = _run(w, kd, vd, kq)
+    toks = [b * 8192 + t for b in range(4) for t in (0, 1, 255, 256, 4095, 8191)]
+    _check(got, _ref(w, kc, vc, ks, vs, tokens=toks), tokens=toks, label="4x8192 int8 prefill (sampled)")
