@@ -62,7 +62,8 @@ def algorithmic_bytes(context_lens, query_lens, num_q_heads, num_kv_heads, head_
     With a sliding window only the positions some row can see count.  A
     quantized cache stores ``kv_code_bytes`` per element plus ``scale_bytes``
     per (position, KV head) vector (page "32. Production attention kernels",
-    Quantized KV caches: 4 extra bytes per 128-value head vector)."""
+    Quantized KV caches: a float32 scale, 4 bytes, beside each vector of D
+    codes)."""
     per_vec = head_dim * (elem_bytes if kv_code_bytes is None else kv_code_bytes) + scale_bytes
     kv = ids = 0
     for L, n in zip(context_lens, query_lens):

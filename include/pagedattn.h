@@ -165,9 +165,9 @@ typedef struct pa_kv_quant {
  *           element type.  Needs dtype PA_BF16 (PA_ERR_UNSUPPORTED
  *           otherwise); the pools and kv strides must be 16-byte aligned in
  *           bytes and the scale pools 4-byte aligned.  The codes are
- *           converted to bf16 in registers, a key's scale multiplies its
- *           scores and a value's scale its probability before the PV
- *           product (decode and verification tiles); prefill tiles
+ *           converted to bf16 in registers, each score is scaled by its
+ *           key's scale and each probability by its value's scale ahead of
+ *           the PV product (decode and verification tiles); prefill tiles
  *           dequantize into bf16 when a block is staged.
  */
 typedef struct pa_attn_opts {
@@ -252,8 +252,7 @@ int32_t pa_choose_splits(const pa_dims* dims);
  * causal (a token with pos < 0 sees nothing); every block-table entry a
  * sequence uses lies in [0, P); and, when slot_mapping is not NULL, every
  * slot is -1 or in [0, P*ps) and no slot repeats (page "Attention and KV
- * Cache": a checked write map refuses a slot outside the pool or named
- * twice).  Returns PA_OK, PA_ERR_INVALID_DATA, or an argument error.
+ * Cache": its checked write map rejects out-of-pool and repeated slots).  Returns PA_OK, PA_ERR_INVALID_DATA, or an argument error.
  */
 pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* query_start_loc, const int32_t* slot_mapping,

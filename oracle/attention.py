@@ -19,7 +19,7 @@ Cache", Multi-head, GQA, and MQA: kv_head = q_head / n_rep).
 
 The visible keys are ``J = {j in [0, L) : not causal or j <= pos}``; key j lives
 at pool page ``block_tables[b, j // ps]``, slot ``j % ps`` (page "32. Production
-attention kernels", the block table is the only indirection; page
+attention kernels", pages are reached through the block table alone; page
 "paged-attn-xpu", cache layout ``[num_blocks, block_size, num_kv_heads,
 head_size]``).  With ``x_j = scale * q . k_j`` the output is
 ``sum_J exp(x_j - max x) v_j / sum_J exp(x_j - max x)`` (page "Attention and KV
@@ -92,8 +92,8 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
                   chunk: int = 1024, window: int = 0, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Gather-then-dense attention in float64.
 
-    Follows page "paged-attn-xpu" (the dense reference that gathers each
-    sequence's pages and runs softmax in float64) and the reference backend of
+    Follows page "paged-attn-xpu" (its validation compares against a dense
+    float64 computation over the sequence's gathered pages) and the reference backend of
     page "32. Production attention kernels" (gather blocks, repeat KV heads over
     the group, dense causal attention).  Query rows are processed in chunks of
     ``chunk`` tokens only to bound memory; each row's result is the definition.

@@ -14,17 +14,16 @@ caches; page "Attention kernels", INT8 cache):
   element lands on the code range's edge, so nothing overflows).  Every step
   is a float32 operation in this order, so a kernel that takes the same steps
   in float32 reproduces the codes and scales bit for bit.
-* Key smoothing (page "Attention kernels", INT8 cache: the queries are
-  multiplied by the keys' smoothing factors, which undoes the smoothing in the
-  scores): with per-channel factors ``smooth [Hkv, D]`` keys are divided by
-  them (float32) before quantization.  The key a cached code stands for is
+* Key smoothing (page "Attention kernels", INT8 cache: smoothing of the keys
+  is compensated on the query side): with per-channel factors
+  ``smooth [Hkv, D]`` keys are divided by them (float32) before quantization.  The key a cached code stands for is
   then ``code * scale * smooth``, and the scores are unchanged:
   ``q . (k / s * s) = (q * s) . (k / s)``.  No smoothing means factors of 1.
 * The cache is read back as ``code * scale`` (times ``smooth`` for keys),
-  exactly, in float64; attention over those dequantized values is the
-  target the quantized kernels are compared with (page "32. Production
-  attention kernels", The tests and the measurements: INT8 and FP8 caches
-  match the reference on the dequantized values).
+  exactly, in float64; attention over that read-back is the target the
+  quantized kernels are compared with (page "32. Production attention
+  kernels", The tests and the measurements: the INT8 and FP8 caches are
+  checked against a reference computed from what the cache stores).
 """
 from __future__ import annotations
 

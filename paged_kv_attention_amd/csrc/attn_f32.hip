@@ -213,7 +213,7 @@ hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st) {
 // KV write: token i's K and V rows ([Hkv, D]) go to flat slot s =
 // slot_mapping[i] = page * ps + offset of both pools; s < 0 writes nothing
 // (page "Attention and KV Cache", Paged KV: the write map, -1 for padding
-// tokens; cost follows the tokens, not the pool).  One workgroup per token,
+// tokens; the work scales with the step's tokens, never with the pool size).  One workgroup per token,
 // 16-byte copies; slots outside the pool are skipped.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteParams p) {

@@ -38,9 +38,10 @@
 // Quantized pools (page "Attention kernels", INT8 cache; page "32.
 // Production attention kernels", Quantized KV caches): K and V hold 1-byte
 // int8 or float8 E4M3 codes with one float32 scale per (slot, KV head).  The
-// codes are converted to bf16 in registers (exactly), a key's scale
-// multiplies its scores, a value's scale its probability before the PV
-// product, and the query is multiplied by the keys' smoothing factors once.
+// codes are converted to bf16 in registers (exactly), each score is scaled
+// by its key's scale and each probability by its value's scale ahead of the
+// PV product, and the per-channel key smoothing is moved onto the query
+// once, where it cancels in every score.
 // A chunk's 64 scales go through a small LDS area of the wave.
 //
 // The four waves' states are merged in LDS in a fixed order.  With one split
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) qB[nt][s] = *(const bf16x8*)(qp + 32 * s + 8 * q4);
       if (QUANT && p.k_smooth) {
-        // q times the keys' smoothing factors undoes the smoothing in the scores
+        // scaling q per channel by the key smoothing cancels it in q . k
         const float* sm = p.k_smooth + (int64_t)g * D;
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) {

@@ -15,8 +15,8 @@
 // Per block and wave:
 //   S^T[64 keys x 32 rows] = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS);
 //   mask only blocks that reach the diagonal or the context end (page
-//   "Attention kernels", Walking the block table: only pages that overlap the
-//   diagonal are masked);
+//   "Attention kernels", Walking the block table: masking is confined to the
+//   pages the diagonal crosses);
 //   online softmax in float32 with exp2; the scale*log2(e) factor and the
 //   running max meet in one FMA per score (page "Attention kernels", One
 //   kernel family).  The reference max of a row only moves when a block's max
@@ -38,7 +38,7 @@
 // Quantized pools (page "Attention kernels", INT8 cache): a block's 1-byte
 // codes are loaded (half the bytes), multiplied by their key's scale and
 // rounded to bf16 when the block is staged in LDS, so the loop itself is the
-// bf16 one; the query is multiplied by the keys' smoothing factors once.
+// bf16 one; the per-channel key smoothing is moved onto the query once.
 //
 // Tiles with more keys run first (page "Attention kernels", Open questions:
 // heaviest causal blocks first), and the flat block index is remapped so
@@ -150,7 +150,7 @@ void prefill_kernel(const AttnParams p) {
       qB[s] = __builtin_bit_cast(bf16x8, w);
     }
     if (KQ != KV_BF16 && p.k_smooth) {
-      // q times the keys' smoothing factors undoes the smoothing in the scores
+      // scaling q per channel by the key smoothing cancels it in q . k
       const float* sm = p.k_smooth + (int64_t)g * D + 8 * h2;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) {

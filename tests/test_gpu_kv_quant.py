@@ -1,6 +1,7 @@
 """GPU parity of the quantized KV cache (page "32. Production attention
 kernels", Quantized KV caches and its tests: INT8 and FP8 caches match the
-reference on the dequantized values; page "Attention kernels", INT8 cache).
+reference computed from what the cache stores; page "Attention kernels",
+INT8 cache).
 
 * kv_cache_write_quant produces the oracle's codes and scales bit for bit
   (integer and byte work), for int8 and fp8, bf16 and float32 inputs, with

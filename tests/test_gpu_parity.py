@@ -2,11 +2,10 @@
 
 Bar: max abs error <= 1e-5 for float32 inputs and <= 2e-2 for bf16 inputs
 (fp32 accumulation), no NaN or Inf in any written row.  The cases follow the
-pages' own test lists: a mixed batch in every state, grouped heads with
-group sizes 4 and 3 and plain multi-head attention, split-KV with 1, 3 and 8
-splits (page "32. Production attention kernels", The tests and the
-measurements); head sizes 64/128/256, ragged contexts spanning many pages,
-contexts of 600 and 1500 split vs unsplit, empty contexts giving zeros and a
+pages' own test lists: a mixed batch covering every request state, GQA at
+group 4, group 3 and MHA, and several split counts (page "32. Production
+attention kernels", The tests and the measurements); head sizes 64/128/256, ragged contexts spanning many pages,
+split and unsplit runs of a few-hundred and a thousand-plus key context, empty contexts giving zeros and a
 constant V returning the constant (page "paged-attn-xpu", Validation).
 """
 import dataclasses

@@ -1,7 +1,8 @@
 """hipGraph capture and replay of one decode step (KV write + attention) while
 the sequences grow: positions, lengths, page ids and write slots live in
 device buffers, so the captured launches stay valid (page "Attention kernels",
-Walking the block table: a captured graph stays valid as the sequence grows).
+Walking the block table: a graph captured once keeps working while contexts
+grow).
 Every replay is checked against the float64 oracle, with eager work between
 replays."""
 import pytest
