@@ -154,6 +154,57 @@ def make_custom(*, seed: int, context_lens: List[int], query_lens: List[int], nu
                     scale=sc, causal=causal)
 
 
+def make_shared_prefix(*, seed: int, prefix_len: int, suffix_lens: List[int], query_lens: List[int],
+                       num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                       dtype: torch.dtype = torch.bfloat16, name: str = "shared prefix") -> Workload:
+    """Requests that share their first ``prefix_len`` cached positions.
+
+    ``prefix_len`` is a whole number of pages.  The prefix pages are drawn once
+    and every block table starts with the same page ids (a cached system
+    prompt, page "32. Production attention kernels", Stretch exercises:
+    cascade attention); request b then owns ``suffix_lens[b]`` further
+    positions (its step's ``query_lens[b]`` tokens included) on pages of its
+    own.  Draw order: (1) pool permutation, (2) q, (3) k_pool, (4) v_pool.
+    """
+    assert prefix_len % page_size == 0 and prefix_len > 0
+    gen = torch.Generator("cpu").manual_seed(seed)
+    B = len(suffix_lens)
+    assert len(query_lens) == B and all(n <= s for n, s in zip(query_lens, suffix_lens))
+    npre = prefix_len // page_size
+    nsuf = [(s + page_size - 1) // page_size for s in suffix_lens]
+    P = npre + sum(nsuf)
+    W = npre + max(nsuf)
+    perm = torch.randperm(P, generator=gen).to(torch.int32)
+    bt = torch.zeros(B, W, dtype=torch.int32)
+    off = npre
+    for b in range(B):
+        bt[b, :npre] = perm[:npre]
+        bt[b, npre:npre + nsuf[b]] = perm[off:off + nsuf[b]]
+        off += nsuf[b]
+    N = sum(query_lens)
+    q = _draw(gen, (N, num_q_heads, head_dim), dtype)
+    k_pool = _draw(gen, (P, page_size, num_kv_heads, head_dim), dtype)
+    v_pool = _draw(gen, (P, page_size, num_kv_heads, head_dim), dtype)
+    qsl = torch.zeros(B + 1, dtype=torch.int32)
+    qsl[1:] = torch.cumsum(torch.tensor(query_lens, dtype=torch.int64), 0).to(torch.int32)
+    lens = torch.tensor([prefix_len + s for s in suffix_lens], dtype=torch.int32)
+    return Workload(name=name, dtype=dtype, q=q, k_pool=k_pool, v_pool=v_pool, block_tables=bt,
+                    context_lens=lens, query_start_loc=qsl, scale=_f32(1.0 / math.sqrt(head_dim)))
+
+
+def make_cascade_decode(seed: int = 7) -> Workload:
+    """64 decoding requests sharing a 4,096-position cached prefix (64 pages
+    of 64), each with its own suffix of U{1..512} positions; 32 query / 8 KV
+    heads, head dim 128, bf16 (the shared-system-prompt case of page "32.
+    Production attention kernels", Stretch exercises: cascade attention, with
+    its ~4,000-token prompt rounded to whole pages)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    suffix = torch.randint(1, 513, (64,), generator=gen).tolist()
+    return make_shared_prefix(seed=seed + 1000, prefix_len=4096, suffix_lens=suffix, query_lens=[1] * 64,
+                              num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+                              name="cascade decode: 64 requests, shared 4096-position prefix, suffixes U{1..512}")
+
+
 def make(config: int, seed: Optional[int] = None, *, padded_width: bool = False) -> Workload:
     """The five measured workloads (6 = the head-dim-256 prefill variant).
 
