@@ -169,20 +169,36 @@ typedef struct pa_kv_quant {
  *           key's scale and each probability by its value's scale ahead of
  *           the PV product (decode and verification tiles); prefill tiles
  *           dequantize into bf16 when a block is staged.
+ *   shared_prefix_len  Cascade attention (page "32. Production attention
+ *           kernels", Stretch exercises: cascade attention): when > 0, every
+ *           sequence's first shared_prefix_len positions are the same cached
+ *           keys on the same pages (block_tables[b][0 .. len/ps) equal for
+ *           all b; len a multiple of ps), and every query token sits after
+ *           them (L_b - n_b >= len; pa_validate_opts checks both).  The
+ *           prefix's K/V is then read once for the whole batch by MFMA
+ *           tiles over all query tokens, each sequence attends its own
+ *           suffix, and the two partial results are merged by their
+ *           log-sum-exp.  The result equals the plain call's.  Needs dtype
+ *           PA_BF16, no window, and max_query_len within the decode /
+ *           verification class (n*G <= 64, n <= 16); PA_ERR_UNSUPPORTED
+ *           otherwise.  Its workspace is pa_workspace_size_opts().
  */
 typedef struct pa_attn_opts {
   int32_t window;
   int32_t reserved0;       /* must be 0 */
   const float* sinks;
   const pa_kv_quant* kv_quant;
+  int32_t shared_prefix_len;
+  int32_t reserved1;       /* must be 0 */
 } pa_attn_opts;
 
 /*
  * paged_attention_opts -- paged_attention with the options above.  Every
  * other argument, the layouts and the error behaviour are those of
  * paged_attention, which is this call with opts == NULL.  The workspace
- * pa_workspace_size(dims, dtype) returns is enough for any options (a window
- * only lowers the split count).
+ * needed is pa_workspace_size_opts(dims, dtype, opts); without a shared
+ * prefix it never exceeds pa_workspace_size(dims, dtype) (a window only
+ * lowers the split count).
  */
 pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_tables, const int32_t* context_lens,
@@ -235,6 +251,14 @@ pa_status kv_cache_write_quant(const void* k_new, const void* v_new, void* k_cod
 size_t pa_workspace_size(const pa_dims* dims, pa_dtype dtype);
 
 /*
+ * pa_workspace_size_opts -- the same for paged_attention_opts: with a shared
+ * prefix, (Sp + Ss) * N * Hq * (D + 2) * 4 bytes, Sp the prefix key ranges
+ * and Ss the suffix splits; otherwise pa_workspace_size.  0 for invalid
+ * arguments.
+ */
+size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn_opts* opts);
+
+/*
  * pa_choose_splits -- the split count paged_attention will use for decode
  * rows (one token, or n*G <= 16 rows): dims->num_splits when > 0, else enough
  * workgroups to fill every CU of the current device with at least 256 keys
@@ -257,6 +281,16 @@ int32_t pa_choose_splits(const pa_dims* dims);
 pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* query_start_loc, const int32_t* slot_mapping,
                       int32_t num_slots, int causal, const pa_dims* dims, void* stream);
+
+/*
+ * pa_validate_opts -- pa_validate plus the contract of the options: with a
+ * shared prefix of len positions, every sequence's first len/ps table entries
+ * equal sequence 0's and L_b - n_b >= len.  SYNCHRONOUS, debug and test only.
+ */
+pa_status pa_validate_opts(const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* query_start_loc, const int32_t* slot_mapping,
+                           int32_t num_slots, int causal, const pa_dims* dims, const pa_attn_opts* opts,
+                           void* stream);
 
 /* pa_status_string -- static human-readable text for a status code. */
 const char* pa_status_string(pa_status status);

@@ -21,7 +21,8 @@ PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_L
 PA_F32, PA_BF16 = 0, 1
 
 EXPORTED = ("paged_attention", "paged_attention_opts", "kv_cache_write", "kv_cache_write_quant", "pa_workspace_size",
-            "pa_choose_splits", "pa_validate", "pa_status_string", "pa_device_cu_count")
+            "pa_workspace_size_opts", "pa_choose_splits", "pa_validate", "pa_validate_opts", "pa_status_string",
+            "pa_device_cu_count")
 
 
 class PaDims(ctypes.Structure):
@@ -45,7 +46,8 @@ class PaKvQuant(ctypes.Structure):
 
 class PaAttnOpts(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("sinks", ctypes.c_void_p),
-                ("kv_quant", ctypes.POINTER(PaKvQuant))]
+                ("kv_quant", ctypes.POINTER(PaKvQuant)), ("shared_prefix_len", ctypes.c_int32),
+                ("reserved1", ctypes.c_int32)]
 
 
 PA_KV_INT8, PA_KV_FP8_E4M3 = 1, 2
@@ -132,6 +134,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    ctypes.POINTER(PaDims), ctypes.c_int, vp]
     lib.pa_workspace_size.restype = ctypes.c_size_t
     lib.pa_workspace_size.argtypes = [ctypes.POINTER(PaDims), ctypes.c_int]
+    lib.pa_workspace_size_opts.restype = ctypes.c_size_t
+    lib.pa_workspace_size_opts.argtypes = [ctypes.POINTER(PaDims), ctypes.c_int, ctypes.POINTER(PaAttnOpts)]
+    lib.pa_validate_opts.restype = ctypes.c_int
+    lib.pa_validate_opts.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(PaDims),
+                                     ctypes.POINTER(PaAttnOpts), vp]
     lib.pa_choose_splits.restype = ctypes.c_int32
     lib.pa_choose_splits.argtypes = [ctypes.POINTER(PaDims)]
     lib.pa_validate.restype = ctypes.c_int
@@ -235,7 +242,7 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                     causal: bool = True, *, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, max_query_len: Optional[int] = None,
                     num_splits: int = 0, window: int = 0, sinks: Optional[torch.Tensor] = None,
-                    kv_quant: Optional[KvQuant] = None, stream=None) -> torch.Tensor:
+                    kv_quant: Optional[KvQuant] = None, shared_prefix_len: int = 0, stream=None) -> torch.Tensor:
     """Causal GQA attention of q over the paged pools; returns ``out`` [N, Hq, D].
 
     ``scale`` defaults to 1/sqrt(D).  ``max_query_len`` is a host bound on any
@@ -244,7 +251,8 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     positions) and ``sinks`` a float32 [Hq] device tensor of sink logits; with
     either set the call goes through ``paged_attention_opts``.  With
     ``kv_quant`` the pools are 1-byte code pools (int8 / float8_e4m3fn) and
-    q must be bfloat16.
+    q must be bfloat16.  ``shared_prefix_len`` > 0 runs cascade attention
+    over a prefix every sequence shares (same first pages, queries after it).
     """
     lib = load_library()
     if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
@@ -261,21 +269,25 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     cl = _i32(context_lens, "context_lens")
     qsl = _i32(query_start_loc, "query_start_loc")
     code = _dtype_code(q.dtype)
-    need = int(lib.pa_workspace_size(ctypes.byref(dims), code))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if scale is None:
-        scale = 1.0 / math.sqrt(q.shape[-1])
-    if window or sinks is not None or kv_quant is not None:
+    opts = None
+    if window or sinks is not None or kv_quant is not None or shared_prefix_len:
         if sinks is not None:
             if sinks.dtype != torch.float32 or sinks.device != q.device or sinks.numel() != q.shape[1]:
                 raise ValueError("sinks must be a float32 tensor of num_q_heads values on q's device")
             sinks = sinks.contiguous()
         kq = kv_quant.struct() if kv_quant is not None else None
         opts = PaAttnOpts(int(window), 0, sinks.data_ptr() if sinks is not None else None,
-                          ctypes.pointer(kq) if kq is not None else None)
+                          ctypes.pointer(kq) if kq is not None else None, int(shared_prefix_len), 0)
+        need = int(lib.pa_workspace_size_opts(ctypes.byref(dims), code, ctypes.byref(opts)))
+    else:
+        need = int(lib.pa_workspace_size(ctypes.byref(dims), code))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if opts is not None:
         st = lib.paged_attention_opts(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), bt.data_ptr(),
                                       cl.data_ptr(), qsl.data_ptr(), float(scale), 1 if causal else 0,
                                       out.data_ptr(), ws_ptr, ws_bytes, ctypes.byref(dims), code,
@@ -337,8 +349,9 @@ def kv_cache_write_quant(k_new: torch.Tensor, v_new: torch.Tensor, k_codes: torc
 
 def validate(block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor, *,
              num_tokens: int, page_size: int, num_pages: int, slot_mapping: Optional[torch.Tensor] = None,
-             causal: bool = True, stream=None) -> int:
-    """Synchronous metadata check (debug/test only); returns the status code."""
+             causal: bool = True, window: int = 0, shared_prefix_len: int = 0, stream=None) -> int:
+    """Synchronous metadata check (debug/test only); returns the status code.
+    With ``shared_prefix_len`` it also checks the shared-prefix contract."""
     lib = load_library()
     dims = PaDims()
     dims.num_seqs = int(block_tables.shape[0])
@@ -349,6 +362,8 @@ def validate(block_tables: torch.Tensor, context_lens: torch.Tensor, query_start
     if slot_mapping is not None:
         sm = _i32(slot_mapping, "slot_mapping")
         sm_ptr, ns = sm.data_ptr(), int(sm.numel())
-    return int(lib.pa_validate(_i32(block_tables, "block_tables").data_ptr(), _i32(context_lens, "context_lens").data_ptr(),
-                               _i32(query_start_loc, "query_start_loc").data_ptr(), sm_ptr, ns, 1 if causal else 0,
-                               ctypes.byref(dims), _stream_ptr(stream)))
+    opts = PaAttnOpts(int(window), 0, None, None, int(shared_prefix_len), 0)
+    return int(lib.pa_validate_opts(_i32(block_tables, "block_tables").data_ptr(),
+                                    _i32(context_lens, "context_lens").data_ptr(),
+                                    _i32(query_start_loc, "query_start_loc").data_ptr(), sm_ptr, ns,
+                                    1 if causal else 0, ctypes.byref(dims), ctypes.byref(opts), _stream_ptr(stream)))

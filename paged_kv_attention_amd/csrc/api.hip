@@ -12,6 +12,7 @@
 namespace pa {
 hipError_t launch_decode(const AttnParams& p, int nt, hipStream_t st);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t st);
+hipError_t launch_prefix(const AttnParams& p, hipStream_t st);
 hipError_t launch_f32(const AttnParams& p, int max_q, hipStream_t st);
 hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
@@ -127,6 +128,16 @@ size_t pa_workspace_size(const pa_dims* dims, pa_dtype dtype) {
   return make_plan(dims, dtype, cu_count()).workspace_bytes;
 }
 
+size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn_opts* opts) {
+  if (check_dims(dims, dtype) != PA_OK) return 0;
+  const int window = opts && opts->window > 0 ? opts->window : 0;
+  if (opts && opts->shared_prefix_len > 0) {
+    const CascadePlan cp = make_cascade_plan(dims, dtype, cu_count(), opts->shared_prefix_len, window);
+    return cp.status == PA_OK ? cp.workspace_bytes : 0;
+  }
+  return make_plan(dims, dtype, cu_count(), window).workspace_bytes;
+}
+
 pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                           const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
                           void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims, pa_dtype dtype,
@@ -144,7 +155,8 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   if (!isfinite(scale)) return PA_ERR_SHAPE;
   const int window = opts ? opts->window : 0;
   const float* sinks = opts ? opts->sinks : nullptr;
-  if (window < 0 || (opts && opts->reserved0 != 0)) return PA_ERR_SHAPE;
+  const int prefix_len = opts ? opts->shared_prefix_len : 0;
+  if (window < 0 || prefix_len < 0 || (opts && (opts->reserved0 != 0 || opts->reserved1 != 0))) return PA_ERR_SHAPE;
   if (sinks && ((uintptr_t)sinks & 3u)) return PA_ERR_UNSUPPORTED;
   const pa_kv_quant* kq = opts ? opts->kv_quant : nullptr;
   if (kq) {
@@ -156,8 +168,13 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_UNSUPPORTED;
   if (kq && (!kq->k_scale || !kq->v_scale)) return PA_ERR_NULL;
   const Plan pl = make_plan(dims, dtype, cu_count(), window);
-  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes || !aligned16(workspace)))
-    return PA_ERR_WORKSPACE;
+  CascadePlan cp{};
+  if (prefix_len > 0) {
+    cp = make_cascade_plan(dims, dtype, cu_count(), prefix_len, window);
+    if (cp.status != PA_OK) return cp.status;
+  }
+  const size_t need = prefix_len > 0 ? cp.workspace_bytes : pl.workspace_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_WORKSPACE;
 
   AttnParams p{};
   p.q = q;
@@ -216,6 +233,52 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  if (prefix_len > 0) {
+    // cascade: prefix pass over all query tokens (split slots 0..Sp-1), the
+    // sequences' own suffixes (slots Sp..Sp+Ss-1), then one combine of all
+    // partials per row; workspace rows are flat tokens
+    const int slots = cp.prefix_splits + cp.suffix_splits;
+    p.ws_acc = (float*)workspace;
+    p.ws_ml = (float*)workspace + (size_t)slots * N * Hq * dims->head_dim;
+    p.ws_flat = 1;
+    p.comb_splits_small = p.comb_splits_big = slots;
+    p.comb_max_n = pl.dec_max_n;
+    p.comb_tokens = pl.mql < pl.dec_max_n ? pl.mql : pl.dec_max_n;
+    AttnParams pre = p;
+    pre.prefix_len = prefix_len;
+    pre.prefix_splits = cp.prefix_splits;
+    pre.prefix_split_keys = cp.prefix_split_keys;
+    pre.num_qtiles = cp.prefix_qtiles;
+    pre.sinks = nullptr;                       // folded once, by the suffix pass
+    AttnParams suf = p;
+    suf.key_lo = prefix_len;
+    suf.force_partial = 1;
+    suf.split_base = cp.prefix_splits;
+    suf.num_splits = cp.suffix_splits;
+    suf.pages_per_split = cp.suffix_pages_per_split;
+    AttnParams q1 = suf, q2 = suf;
+    q1.row_lo = 0;
+    q1.row_hi = 16;
+    q2.row_lo = 16;
+    q2.row_hi = 16 * pl.big_nt;
+    SideStreams* ss = lock_side_streams(s);
+    bool forked = false;
+    if (ss) {
+      e = hipEventRecord(ss->fork, s);
+      if (e == hipSuccess) forked = (e = hipStreamWaitEvent(ss->side[0], ss->fork, 0)) == hipSuccess;
+    }
+    if (e == hipSuccess && cp.prefix_splits > 0) e = launch_prefix(pre, forked ? ss->side[0] : s);
+    if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
+    if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
+    if (forked) {                              // joined even after a failed launch
+      hipError_t j = hipEventRecord(ss->join[0], ss->side[0]);
+      if (j == hipSuccess) j = hipStreamWaitEvent(s, ss->join[0], 0);
+      if (e == hipSuccess) e = j;
+    }
+    if (ss) ss->mu.unlock();
+    if (e == hipSuccess) e = launch_combine(p, true, s);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
   if (dtype == PA_F32) {
     e = launch_f32(p, pl.mql, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, false, s);
@@ -358,6 +421,13 @@ pa_status kv_cache_write_quant(const void* k_new, const void* v_new, void* k_cod
 pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
                       const int32_t* slot_mapping, int32_t num_slots, int causal, const pa_dims* dims,
                       void* stream) {
+  return pa_validate_opts(block_tables, context_lens, query_start_loc, slot_mapping, num_slots, causal, dims,
+                          nullptr, stream);
+}
+
+pa_status pa_validate_opts(const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* query_start_loc, const int32_t* slot_mapping, int32_t num_slots,
+                           int causal, const pa_dims* dims, const pa_attn_opts* opts, void* stream) {
   if (!dims) return PA_ERR_NULL;
   if (dims->num_seqs < 0 || dims->table_width < 0 || dims->num_pages < 0 || num_slots < 0) return PA_ERR_SHAPE;
   if (dims->page_size < 1) return PA_ERR_UNSUPPORTED;
@@ -375,8 +445,11 @@ pa_status pa_validate(const int32_t* block_tables, const int32_t* context_lens, 
   if (e == hipSuccess && num_slots > 0) e = hipMemcpyAsync(sl.data(), slot_mapping, sl.size() * 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
-  return validate_host(bt.data(), lens.data(), qsl.data(), num_slots > 0 ? sl.data() : nullptr, num_slots, causal,
-                       dims);
+  const pa_status st = validate_host(bt.data(), lens.data(), qsl.data(), num_slots > 0 ? sl.data() : nullptr,
+                                     num_slots, causal, dims);
+  if (st != PA_OK || !opts) return st;
+  if (opts->window < 0 || opts->shared_prefix_len < 0) return PA_ERR_SHAPE;
+  return validate_shared_prefix(bt.data(), lens.data(), qsl.data(), opts->shared_prefix_len, dims);
 }
 
 }  // extern "C"

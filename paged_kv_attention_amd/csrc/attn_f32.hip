@@ -161,8 +161,9 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnParams p) {
   const int S = n * p.group <= 16 ? p.comb_splits_small : p.comb_splits_big;
   if (S <= 1) return;
   const int tok = s0 + t;
-  const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
-  const int64_t row = ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
+  // workspace rows per split: (sequence, step token) slots, or flat tokens
+  const int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
+  const int64_t row = p.ws_flat ? (int64_t)tok * p.num_q_heads + h : ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
   float M = kNegInf;
   for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(s * NH + row) * 2]);
   const float Ms = M == kNegInf ? 0.f : M;

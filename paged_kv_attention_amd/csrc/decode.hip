@@ -115,11 +115,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
   const int npages = (L + ps - 1) / ps;
   const int window = WIN ? p.window : 0;
-  // with a sliding window the splits cut the pages from the first token's
-  // window start on, and keys below that start are never loaded
-  const int pg0 = (WIN ? split_page_base(L, n, window, ps) : 0) + split * p.pages_per_split;
+  const int key_lo = WIN ? p.key_lo : 0;
+  // with a lower key bound (a sliding window's start, or the end of a prefix
+  // handled by the cascade's prefix pass) the splits cut the pages from the
+  // tile's lowest bound on, and keys below it are never loaded
+  const int wlo = WIN ? max(window > 0 ? max(0, L - n - window + 1) : 0, key_lo) : 0;
+  const int pg0 = wlo / ps + split * p.pages_per_split;
   const int pg1 = min(pg0 + p.pages_per_split, npages);
-  const int wlo = WIN ? max(0, L - n - window + 1) : 0;
   const int k_begin = WIN ? max(pg0 * ps, wlo & ~15) : pg0 * ps;   // 16-key tiles stay inside pages
   const int k_end = min(pg1 * ps, L);
   const int nchunks = k_end > k_begin ? (k_end - k_begin + C::KC - 1) / C::KC : 0;
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   // keys below mask_lim are visible to every row of this tile, and so are
   // keys at or above win_all (inside the last token's window)
   const int mask_lim = min(k_end, causal ? diag + 1 : L);
-  const int win_all = WIN ? diag + n - window : INT_MIN;
+  const int win_all = WIN ? max(key_lo, window > 0 ? diag + n - window : INT_MIN) : INT_MIN;
 
   // ---- query tile as the B operand of S^T = K . Q^T (row = lane % 16)
   bf16x8 qB[NT][C::DS];
@@ -311,7 +313,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
                     (QUANT ? p.scale_log2 * ksc[t][r] : p.scale_log2);
           if (need_mask) {
             const int j = k0 + 16 * t + 4 * q4 + r;
-            const bool vis = j < k_end && (!causal || j <= diag + tok) && (!WIN || j > diag + tok - window);
+            const bool vis = j < k_end && (!causal || j <= diag + tok) &&
+                             (!WIN || (j >= key_lo && (window <= 0 || j > diag + tok - window)));
             v = vis ? v : kNegInf;
           }
           x[t][r] = v;
@@ -441,7 +444,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   }
 
   const int nrows = min(rows, ROWS);
-  const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
+  // workspace rows per split: (sequence, step token) slots, or flat tokens
+  const int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
   for (int it = threadIdx.x; it < nrows * (D / 4); it += 256) {
     const int row = it / (D / 4), c4 = it % (D / 4);
     const int tok = s0 + row / G, head = g * G + row % G;
@@ -458,12 +462,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       o *= e;
       M = Mn;
     }
-    if (p.num_splits == 1) {
+    if (p.num_splits == 1 && !p.force_partial) {
       const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
       *(u32x2*)op = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
     } else {
-      const int64_t ri = (int64_t)split * NH + ((int64_t)b * p.ws_tok + row / G) * p.num_q_heads + head;
+      const int64_t rrow = p.ws_flat ? (int64_t)tok * p.num_q_heads + head
+                                     : ((int64_t)b * p.ws_tok + row / G) * p.num_q_heads + head;
+      const int64_t ri = (int64_t)(p.split_base + split) * NH + rrow;
       *(f32x4*)(p.ws_acc + ri * D + 4 * c4) = o;
       if (c4 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{M, Lt};
     }
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 template <int D, int NT>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
-  const bool win = p.window > 0;
+  const bool win = p.window > 0 || p.key_lo > 0;
   switch (p.kv_code) {
     case KV_INT8:
       if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_INT8>), grid, dim3(256), 0, st, p);

@@ -138,6 +138,62 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
   return pl;
 }
 
+CascadePlan make_cascade_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int prefix_len, int window) {
+  CascadePlan c{};
+  c.status = PA_OK;
+  const int ps = d->page_size, W = d->table_width, N = d->num_tokens;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (prefix_len < 0 || prefix_len % ps != 0 || (int64_t)prefix_len > (int64_t)W * ps) {
+    c.status = PA_ERR_SHAPE;
+    return c;
+  }
+  const int mql = d->max_query_len > 0 && d->max_query_len < N ? d->max_query_len : N;
+  const int dm = 64 / G < 16 ? 64 / G : 16;
+  // the prefix pass runs on the bf16 MFMA tiles and serves decode and
+  // verification steps; a window would need per-row masks inside the prefix
+  if (dtype != PA_BF16 || window > 0 || mql > dm) {
+    c.status = PA_ERR_UNSUPPORTED;
+    return c;
+  }
+  if (cu_count < 1) cu_count = 1;
+  const int tpt = prefill_tile_rows(d->head_dim) / G;
+  c.prefix_qtiles = (N + tpt - 1) / tpt;
+  const int kb = prefill_block_keys();
+  const int blocks = (prefix_len + kb - 1) / kb;
+  // about half the CUs busy with prefix tiles: more ranges would add more
+  // partial-state traffic than they save in MFMA time
+  const int64_t units = (int64_t)c.prefix_qtiles * d->num_kv_heads;
+  int64_t s = ((int64_t)cu_count / 2 + units - 1) / units;
+  if (s > blocks) s = blocks;
+  if (s < 1) s = 1;
+  const int per = (int)((blocks + s - 1) / s);
+  c.prefix_split_keys = per * kb;
+  c.prefix_splits = blocks > 0 ? (blocks + per - 1) / per : 0;
+  pa_dims suf = *d;
+  suf.table_width = W - prefix_len / ps > 0 ? W - prefix_len / ps : 1;
+  const int S = choose_splits(&suf, PA_BF16, cu_count);
+  c.suffix_pages_per_split = (suf.table_width + S - 1) / S;
+  c.suffix_splits = (suf.table_width + c.suffix_pages_per_split - 1) / c.suffix_pages_per_split;
+  c.workspace_bytes = (size_t)(c.prefix_splits + c.suffix_splits) * (size_t)N * (size_t)d->num_q_heads *
+                      ((size_t)d->head_dim + 2) * 4;
+  return c;
+}
+
+pa_status validate_shared_prefix(const int32_t* bt, const int32_t* lens, const int32_t* qsl, int prefix_len,
+                                 const pa_dims* d) {
+  if (prefix_len <= 0) return PA_OK;
+  const int B = d->num_seqs, W = d->table_width, ps = d->page_size;
+  if (prefix_len % ps != 0 || (int64_t)prefix_len > (int64_t)W * ps) return PA_ERR_INVALID_DATA;
+  const int npg = prefix_len / ps;
+  for (int b = 0; b < B; ++b) {
+    const int n = qsl[b + 1] - qsl[b];
+    if (lens[b] - n < prefix_len) return PA_ERR_INVALID_DATA;
+    for (int j = 0; j < npg; ++j)
+      if (bt[(int64_t)b * W + j] != bt[j]) return PA_ERR_INVALID_DATA;
+  }
+  return PA_OK;
+}
+
 pa_status validate_host(const int32_t* bt, const int32_t* lens, const int32_t* qsl, const int32_t* slots,
                         int32_t num_slots, int causal, const pa_dims* d) {
   const int B = d->num_seqs, W = d->table_width, ps = d->page_size, P = d->num_pages;

@@ -50,6 +50,24 @@ int window_pages(int window, int mql, int page_size, int W);
 // token's window start (the kernels find that page from the device lengths).
 Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window = 0);
 
+// Cascade plan (a prefix of prefix_len positions shared by every sequence):
+// the prefix pass cuts the prefix into prefix_splits key ranges of
+// prefix_split_keys (a multiple of the prefill block) over prefix_qtiles tiles
+// of the flat token range; the suffix pass splits the remaining table pages
+// as a decode call would.  status is PA_OK or why the cascade cannot run.
+struct CascadePlan {
+  pa_status status;
+  int prefix_splits, prefix_split_keys, prefix_qtiles;
+  int suffix_splits, suffix_pages_per_split;
+  size_t workspace_bytes;  // (prefix_splits + suffix_splits) * N * Hq * (D + 2) * 4
+};
+CascadePlan make_cascade_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int prefix_len, int window);
+
+// Shared-prefix contract on copied metadata: table rows agree with row 0 on
+// the prefix's pages and every query token sits after the prefix.
+pa_status validate_shared_prefix(const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start_loc, int prefix_len, const pa_dims* d);
+
 // Host-side check of copied metadata (the body of pa_validate).
 pa_status validate_host(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
                         const int32_t* slot_mapping, int32_t num_slots, int causal, const pa_dims* d);

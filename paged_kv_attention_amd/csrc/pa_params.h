@@ -11,6 +11,9 @@ namespace pa {
 // Query rows per prefill workgroup tile (32 per wave): 8 waves for head_dim
 // <= 128, 4 waves for 256 (its accumulator does not fit two waves per SIMD).
 constexpr int prefill_tile_rows(int head_dim) { return head_dim <= 128 ? 256 : 128; }
+// Keys per K/V block of the prefill kernel (also the granule of the
+// cascade's prefix key ranges).
+constexpr int prefill_block_keys() { return 64; }
 
 struct AttnParams {
   const void* q;
@@ -49,6 +52,14 @@ struct AttnParams {
   const float* v_scale;
   int64_t sc_stride_page, sc_stride_slot, sc_stride_head;
   const float* k_smooth;
+  // cascade (a prefix shared by every sequence of the batch):
+  int32_t key_lo;           // decode: keys below key_lo are left to the prefix pass (0 = none)
+  int32_t split_base;       // decode: its partials take split slots split_base + split
+  int32_t force_partial;    // decode: write partials even with one split
+  int32_t ws_flat;          // workspace rows indexed by flat token (N * Hq per split)
+  int32_t prefix_len;       // prefix pass: keys [0, prefix_len) of block-table row 0
+  int32_t prefix_splits;    // prefix pass: key ranges, each prefix_split_keys long
+  int32_t prefix_split_keys;
 };
 
 // First page of the split ranges of a sequence with context L and n step

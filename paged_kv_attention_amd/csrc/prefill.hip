@@ -85,26 +85,43 @@ struct PrefillRegs {
 
 // WIN: the launch has a sliding window (p.window > 0); KQ: the pools' code
 // type (KvCode).  The plain instantiation carries none of their code.
-template <int D, int NW, int PF, int KB, bool WIN, int KQ>
+// CAS: the cascade's prefix pass.  The tiles then cover every query token of
+// the batch as one flat, non-causal sequence over the shared prefix (keys
+// [0, p.prefix_len) of block-table row 0, read once for all requests; page
+// "32. Production attention kernels", Stretch exercises: cascade attention),
+// each workgroup takes one key range of the prefix, and the unnormalised
+// state (acc, m, l) goes to the split workspace for the combine.
+template <int D, int NW, int PF, int KB, bool WIN, int KQ, bool CAS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void prefill_kernel(const AttnParams p) {
   using C = PrefillCfg<D, NW, PF, KB>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
-  // ---- XCD-aware block order: consecutive logical tiles share an XCD
-  const int total = gridDim.x;
-  const int id = blockIdx.x;
-  const int xcd = id & 7, per = total >> 3, rem = total & 7;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + (id >> 3);
-  const int nqt = p.num_qtiles;
-  const int qt = nqt - 1 - logical % nqt;       // heaviest tile of a sequence first
-  const int rest = logical / nqt;
-  const int g = rest % p.num_kv_heads;
-  const int b = rest / p.num_kv_heads;
+  int b, g, qt, split = 0;
+  if constexpr (CAS) {
+    // prefix pass: block = (key range, KV head, token tile); all tiles weigh the same
+    const int id = blockIdx.x;
+    split = id % p.prefix_splits;
+    const int rest = id / p.prefix_splits;
+    g = rest % p.num_kv_heads;
+    qt = rest / p.num_kv_heads;
+    b = 0;                                      // the prefix's pages come from table row 0
+  } else {
+    // ---- XCD-aware block order: consecutive logical tiles share an XCD
+    const int total = gridDim.x;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, per = total >> 3, rem = total & 7;
+    const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + (id >> 3);
+    const int nqt = p.num_qtiles;
+    qt = nqt - 1 - logical % nqt;               // heaviest tile of a sequence first
+    const int rest = logical / nqt;
+    g = rest % p.num_kv_heads;
+    b = rest / p.num_kv_heads;
+  }
 
-  const int s0 = p.query_start_loc[b];
-  const int n = p.query_start_loc[b + 1] - s0;
-  if (n <= p.dec_max_n) return;                 // decode class (or empty)
+  const int s0 = CAS ? 0 : p.query_start_loc[b];
+  const int n = CAS ? p.num_tokens : p.query_start_loc[b + 1] - s0;
+  if (!CAS && n <= p.dec_max_n) return;         // decode class (or empty)
   const int G = p.group;
   const int TPT = p.tok_per_tile;
   const int t0 = qt * TPT;
@@ -113,8 +130,11 @@ void prefill_kernel(const AttnParams p) {
   const int rows_valid = tcount * G;
 
   const int ps = p.page_size, psh = p.page_shift;
-  const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
-  const int causal = p.causal;
+  // prefix pass: this workgroup's key range [k_lo, L) of the prefix
+  const int k_lo = CAS ? split * p.prefix_split_keys : 0;
+  const int L = CAS ? min(k_lo + p.prefix_split_keys, p.prefix_len)
+                    : clampi(p.context_lens[b], 0, p.table_width * ps);
+  const int causal = CAS ? 0 : p.causal;
   const int diag = L - n;
   const int k_hi = causal ? clampi(diag + t0 + tcount, 0, L) : L;   // keys any row can see
   const int full_lim = causal ? clampi(diag + t0 + 1, 0, L) : L;    // keys every row sees
@@ -122,7 +142,7 @@ void prefill_kernel(const AttnParams p) {
   // sliding window: blocks before the first row's window start are skipped,
   // and keys below the last row's window start need the window mask
   const int window = WIN ? p.window : 0;
-  const int wlo_tile = WIN ? max(0, diag + t0 - window + 1) : 0;   // first row's window start
+  const int wlo_tile = WIN ? max(0, diag + t0 - window + 1) : (CAS ? k_lo : 0);   // first row's lowest key
   const int blk0 = wlo_tile / C::KB;
   const int win_all = WIN ? diag + t0 + tcount - window : INT_MIN;
 
@@ -202,7 +222,7 @@ void prefill_kernel(const AttnParams p) {
         const int lp = jw >> psh;
         const int pg = page_of(p, b, lp);
         const int64_t pbase = (int64_t)pg * p.kv_stride_page;
-        if (j < L && (!WIN || j >= wlo_tile)) {
+        if (j < L && ((!WIN && !CAS) || j >= wlo_tile)) {
           const int64_t off = pbase + (int64_t)(j - (lp << psh)) * p.kv_stride_slot + 8 * cc;   // elements
           if constexpr (KQ == KV_BF16) {
             r.k[i] = *(const u32x4*)(kbase + off);
@@ -400,6 +420,23 @@ void prefill_kernel(const AttnParams p) {
 
   // ---- normalise and write this lane's row (dims 32*dt + 8*(r/4) + 4*h2 + r%4)
   l_run = xor32_sum(l_run);
+  if constexpr (CAS) {
+    // prefix pass: the unnormalised state of the row for the combine (m in
+    // log2 units, the reference the probabilities were taken against)
+    if (row_ok) {
+      const int64_t NH = (int64_t)p.num_tokens * p.num_q_heads;
+      const int64_t ri = (int64_t)split * NH + (int64_t)(s0 + my_tok) * p.num_q_heads + my_head;
+      float* wa = p.ws_acc + ri * D + 4 * h2;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(wa + 32 * dt + 8 * r4) = f32x4{acc[dt][4 * r4], acc[dt][4 * r4 + 1], acc[dt][4 * r4 + 2],
+                                                   acc[dt][4 * r4 + 3]};
+      if (h2 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{m_run, l_run};
+    }
+    return;
+  }
   if (p.sinks) {
     // the row's sink is one more score with no value row
     const float s2 = row_ok ? p.sinks[my_head] * kLog2e : kNegInf;
@@ -434,6 +471,8 @@ template <> struct PrefillShape<256> { static constexpr int NW = 4, PF = 1, KB =
 static_assert(32 * PrefillShape<64>::NW == prefill_tile_rows(64), "host and kernel tile rows differ");
 static_assert(32 * PrefillShape<128>::NW == prefill_tile_rows(128), "host and kernel tile rows differ");
 static_assert(32 * PrefillShape<256>::NW == prefill_tile_rows(256), "host and kernel tile rows differ");
+static_assert(PrefillShape<64>::KB == prefill_block_keys() && PrefillShape<128>::KB == prefill_block_keys() &&
+              PrefillShape<256>::KB == prefill_block_keys(), "host and kernel block keys differ");
 
 template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
@@ -455,6 +494,30 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
       else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16>), grid, block, 0, st, p);
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefix_t(const AttnParams& p, hipStream_t st) {
+  constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF, KB = PrefillShape<D>::KB;
+  const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.prefix_splits;
+  const dim3 grid((unsigned)total), block(64 * NW);
+  switch (p.kv_code) {
+    case KV_INT8: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_INT8, true>), grid, block, 0, st, p); break;
+    case KV_FP8: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_FP8, true>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16, true>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+// The cascade's prefix pass (see CAS above); p.num_qtiles counts the tiles
+// of the flat token range.
+hipError_t launch_prefix(const AttnParams& p, hipStream_t st) {
+  switch (p.head_dim) {
+    case 64: return launch_prefix_t<64>(p, st);
+    case 128: return launch_prefix_t<128>(p, st);
+    case 256: return launch_prefix_t<256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill(const AttnParams& p, hipStream_t st) {

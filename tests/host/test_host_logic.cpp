@@ -42,6 +42,27 @@ int main() {
   CHECK(pa::split_page_base(4096, 1, 1024, 64) == 48 && pa::split_page_base(4096, 1, 0, 64) == 0);
   CHECK(pa::split_page_base(100, 1, 1024, 64) == 0 && pa::split_page_base(1025, 1, 1024, 64) == 0);
   CHECK(pa::split_page_base(1089, 1, 1024, 64) == 1);
+  // cascade: 64 decodes over a 4096-position shared prefix, suffixes up to 8 pages
+  pa_dims cc = dims(64, 64, 1, 32, 8, 128, 64, 362, 72);
+  pa::CascadePlan cpl = pa::make_cascade_plan(&cc, PA_BF16, 256, 4096, 0);
+  CHECK(cpl.status == PA_OK && cpl.prefix_qtiles == 1 && cpl.prefix_splits == 16 && cpl.prefix_split_keys == 256);
+  CHECK(cpl.suffix_splits == 1 && cpl.suffix_pages_per_split == 8);
+  CHECK(cpl.workspace_bytes == (size_t)17 * 64 * 32 * 130 * 4);
+  CHECK(pa::make_cascade_plan(&cc, PA_BF16, 256, 4000, 0).status == PA_ERR_SHAPE);       // not whole pages
+  CHECK(pa::make_cascade_plan(&cc, PA_BF16, 256, 4096, 512).status == PA_ERR_UNSUPPORTED);   // with a window
+  CHECK(pa::make_cascade_plan(&cc, PA_F32, 256, 4096, 0).status == PA_ERR_UNSUPPORTED);
+  pa_dims cpf = dims(2, 100, 50, 32, 8, 128, 64, 362, 72);                              // prefill-class steps
+  CHECK(pa::make_cascade_plan(&cpf, PA_BF16, 256, 4096, 0).status == PA_ERR_UNSUPPORTED);
+  {
+    // contract: rows share the prefix pages and every token sits after the prefix
+    const int32_t bt[6] = {5, 6, 1, 5, 6, 2}, lens[2] = {9, 10}, qsl[3] = {0, 1, 3};
+    pa_dims dv = dims(2, 3, 2, 4, 2, 64, 4, 8, 3);
+    CHECK(pa::validate_shared_prefix(bt, lens, qsl, 8, &dv) == PA_OK);
+    const int32_t bt2[6] = {5, 6, 1, 5, 7, 2};
+    CHECK(pa::validate_shared_prefix(bt2, lens, qsl, 8, &dv) == PA_ERR_INVALID_DATA);
+    const int32_t lens2[2] = {9, 9};                                                     // token inside the prefix
+    CHECK(pa::validate_shared_prefix(bt, lens2, qsl, 8, &dv) == PA_ERR_INVALID_DATA);
+  }
   // mixed batch: prefill + small and large decode tiles
   pa_dims c4 = dims(32, 547, 512, 32, 8, 128, 64, 2000, 128);
   pa::Plan p4 = pa::make_plan(&c4, PA_BF16, 256);
