@@ -330,6 +330,53 @@ def variant_workloads(steps, warmup):
     return res
 
 
+def cascade_workload(steps, warmup):
+    """64 decoding requests sharing a 4,096-position prefix (suffixes
+    U{1..512}): the cascade call against the plain call on the same inputs,
+    pools rotated over 4 sets.  Algorithmic bytes of the cascade: the
+    prefix's K/V once, every suffix's K/V, q and out, page ids."""
+    import torch
+    import paged_kv_attention_amd as pa
+    from workloads import make_cascade_decode
+    w = make_cascade_decode()
+    dev = torch.device("cuda", 0)
+    q, bt, cl, qsl = w.q.to(dev), w.block_tables.to(dev), w.context_lens.to(dev), w.query_start_loc.to(dev)
+    P, ps, Hkv, D = w.k_pool.shape
+    gen = torch.Generator(device=dev).manual_seed(99)
+    pools = [(pa.pool_like(w.k_pool, dev), pa.pool_like(w.v_pool, dev))]
+    for _ in range(3):
+        k = pa.empty_pool(P, ps, Hkv, D, device=dev)
+        v = pa.empty_pool(P, ps, Hkv, D, device=dev)
+        k.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
+        v.copy_(torch.randn(P, ps, Hkv, D, generator=gen, device=dev))
+        pools.append((k, v))
+    out = torch.empty_like(q)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    prefix = 4096
+    lens = w.context_lens.tolist()
+
+    def run(cascade):
+        def f(i):
+            k, v = pools[i % len(pools)]
+            pa.paged_attention(q, k, v, bt, cl, qsl, w.scale, True, out=out, workspace=ws, max_query_len=1,
+                               shared_prefix_len=prefix if cascade else 0)
+        return f
+    _, per_c = _time_steps([run(True)], steps, warmup)
+    _, per_p = _time_steps([run(False)], steps, warmup)
+    suffix_keys = sum(L - prefix for L in lens)
+    kv_vec = Hkv * D * 2 * 2                                   # K and V bytes per position
+    casc_bytes = (prefix + suffix_keys) * kv_vec + w.num_tokens * w.num_q_heads * D * 2 * 2 + \
+        (prefix // ps + sum((L - prefix + ps - 1) // ps for L in lens)) * 4 + (2 * len(lens) + 1) * 4
+    plain_bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, Hkv, D, ps, 2)
+    gbs = casc_bytes / (per_c[0] * 1e-3) / 1e9
+    return {"workload": w.name, "cascade_ms": round(per_c[0], 5), "plain_ms": round(per_p[0], 5),
+            "speedup": round(per_p[0] / per_c[0], 2), "cascade_algorithmic_bytes": casc_bytes,
+            "plain_algorithmic_bytes": plain_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "plain_GB_s": round(plain_bytes / (per_p[0] * 1e-3) / 1e9, 2), "pool_sets_rotated": len(pools)}
+
+
 def graph_step(db, steps):
     """The decode step (write + attention) captured once in a hipGraph and
     replayed over the rotated pool sets: launch overhead removed."""
@@ -522,6 +569,8 @@ def main():
 
     if args.only is None and not args.no_variants:
         result["variants"] = variant_workloads(args.steps, args.warmup)
+        print("[bench] cascade: 64 requests sharing a 4096-position prefix", file=sys.stderr, flush=True)
+        result["variants"]["cascade_decode"] = cascade_workload(args.steps, args.warmup)
 
     if not args.no_cpu_baseline and args.only is None and decode_w is not None:
         print("[bench] cpu baseline: timing the float64 oracle", file=sys.stderr, flush=True)

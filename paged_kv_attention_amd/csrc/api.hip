@@ -261,22 +261,19 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
     q1.row_hi = 16;
     q2.row_lo = 16;
     q2.row_hi = 16 * pl.big_nt;
-    SideStreams* ss = lock_side_streams(s);
-    bool forked = false;
-    if (ss) {
-      e = hipEventRecord(ss->fork, s);
-      if (e == hipSuccess) forked = (e = hipStreamWaitEvent(ss->side[0], ss->fork, 0)) == hipSuccess;
+    // Launched in order on the caller's stream: the passes are short, and a
+    // fork onto a side stream cost more than their overlap gained.  With a
+    // one-split suffix the decode kernel folds the prefix partials into its
+    // output itself and no combine is launched.
+    const bool fold = cp.suffix_splits == 1;
+    if (fold) {
+      q1.merge_prefix = q2.merge_prefix = cp.prefix_splits;
+      q1.force_partial = q2.force_partial = 0;
     }
-    if (e == hipSuccess && cp.prefix_splits > 0) e = launch_prefix(pre, forked ? ss->side[0] : s);
+    if (cp.prefix_splits > 0) e = launch_prefix(pre, s);
     if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
     if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
-    if (forked) {                              // joined even after a failed launch
-      hipError_t j = hipEventRecord(ss->join[0], ss->side[0]);
-      if (j == hipSuccess) j = hipStreamWaitEvent(s, ss->join[0], 0);
-      if (e == hipSuccess) e = j;
-    }
-    if (ss) ss->mu.unlock();
-    if (e == hipSuccess) e = launch_combine(p, true, s);
+    if (e == hipSuccess && !fold) e = launch_combine(p, true, s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   }
   if (dtype == PA_F32) {

@@ -462,7 +462,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       o *= e;
       M = Mn;
     }
-    if (p.num_splits == 1 && !p.force_partial) {
+    if (p.merge_prefix > 0) {
+      // cascade with a one-split suffix: merge the prefix pass's partials of
+      // this row (flat workspace rows) with the suffix state and normalise
+      const int64_t NHf = (int64_t)p.num_tokens * p.num_q_heads;
+      const int64_t rrow = (int64_t)tok * p.num_q_heads + head;
+      float Mx = M;
+      for (int s2 = 0; s2 < p.merge_prefix; ++s2) Mx = fmaxf(Mx, p.ws_ml[(s2 * NHf + rrow) * 2]);
+      const float Ms = Mx == kNegInf ? 0.f : Mx;
+      const float e0 = fast_exp2(M - Ms);
+      float Ltot = Lt * e0;
+      f32x4 ot = o * e0;
+      for (int s2 = 0; s2 < p.merge_prefix; ++s2) {
+        const int64_t ri = s2 * NHf + rrow;
+        const f32x2 ml = *(const f32x2*)(p.ws_ml + ri * 2);
+        const float w = fast_exp2(ml[0] - Ms);
+        Ltot = fmaf(w, ml[1], Ltot);
+        ot += w * *(const f32x4*)(p.ws_acc + ri * D + 4 * c4);
+      }
+      const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+      __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
+      *(u32x2*)op = u32x2{pack_bf16x2(ot[0] * inv, ot[1] * inv), pack_bf16x2(ot[2] * inv, ot[3] * inv)};
+    } else if (p.num_splits == 1 && !p.force_partial) {
       const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
       *(u32x2*)op = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};

@@ -60,6 +60,8 @@ struct AttnParams {
   int32_t prefix_len;       // prefix pass: keys [0, prefix_len) of block-table row 0
   int32_t prefix_splits;    // prefix pass: key ranges, each prefix_split_keys long
   int32_t prefix_split_keys;
+  int32_t merge_prefix;     // decode with one split: fold this many prefix partials (slots 0..) into
+                            // the output instead of writing a partial
 };
 
 // First page of the split ranges of a sequence with context L and n step
