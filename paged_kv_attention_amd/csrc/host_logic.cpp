@@ -96,8 +96,12 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
     int dm = 64 / G;
     pl.dec_max_n = dm < 16 ? dm : 16;
     const int dmax = pl.mql < pl.dec_max_n ? pl.mql : pl.dec_max_n;
-    pl.dec_small = dmax >= 1 && G <= 16;
-    pl.dec_big = dmax * G > 16;
+    // fewest tokens any sequence can have: the others hold at most mql each
+    // (a batch of equal prefill chunks has no decode-class sequence at all)
+    int64_t nmin = (int64_t)N - (int64_t)(d->num_seqs - 1) * pl.mql;
+    if (nmin < 1) nmin = 1;
+    pl.dec_small = dmax >= 1 && G <= 16 && nmin * G <= 16;
+    pl.dec_big = dmax * G > 16 && nmin <= dmax;
     pl.big_nt = dmax * G <= 32 ? 2 : 4;
     pl.prefill = pl.mql > pl.dec_max_n;
     pl.tok_per_tile = prefill_tile_rows(d->head_dim) / G;
@@ -132,7 +136,7 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
   const int smax = pl.splits > pl.splits_big ? pl.splits : pl.splits_big;
   // split partials are indexed by (sequence, token of the step) over the
   // split classes only, so prefill tokens take no workspace
-  if (smax > 1)
+  if (smax > 1 && pl.combine)
     pl.workspace_bytes = (size_t)smax * (size_t)d->num_seqs * (size_t)pl.ws_tok * (size_t)d->num_q_heads *
                          ((size_t)d->head_dim + 2) * 4;
   return pl;

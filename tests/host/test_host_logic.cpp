@@ -71,15 +71,32 @@ int main() {
   // the verify-tile launch uses 8 splits of 16 pages; partials only for the 16 decode-class token slots
   CHECK(p4.splits == 2 && p4.splits_big == 8 && p4.pages_per_split_big == 16 && p4.ws_tok == 16);
   CHECK(p4.workspace_bytes == (size_t)8 * 32 * 16 * 32 * 130 * 4);
-  // long prefill: no decode rows can split, so prefill tokens take no workspace beyond 16 slots
+  // four equal 8192-token chunks: every sequence is prefill, so no decode
+  // launch, no combine and no workspace
   pa_dims c5 = dims(4, 32768, 8192, 32, 8, 128, 64, 512, 128);
   pa::Plan p5 = pa::make_plan(&c5, PA_BF16, 256);
-  CHECK(p5.prefill && p5.num_qtiles == 128 && p5.ws_tok == 16);
-  CHECK(p5.workspace_bytes == (size_t)p5.splits * 4 * 16 * 32 * 130 * 4 && p5.splits >= p5.splits_big);
-  // a 5-token verify bound: 20 rows -> 32-row tile
-  pa_dims v5 = dims(4, 20, 5, 32, 8, 128, 64, 100, 16);
+  CHECK(p5.prefill && p5.num_qtiles == 128 && !p5.dec_small && !p5.dec_big && !p5.combine);
+  CHECK(p5.workspace_bytes == 0);
+  // one token short of equal chunks: some sequence may have 8191 tokens, still no decode class
+  c5.num_tokens = 32767;
+  CHECK(!pa::make_plan(&c5, PA_BF16, 256).dec_small);
+  // 3 x 8192 + 1: the last sequence may be a decode token
+  c5.num_tokens = 3 * 8192 + 1;
+  pa::Plan p5b = pa::make_plan(&c5, PA_BF16, 256);
+  CHECK(p5b.prefill && p5b.dec_small && p5b.dec_big && p5b.combine);
+  CHECK(p5b.workspace_bytes == (size_t)p5b.splits * 4 * 16 * 32 * 130 * 4 && p5b.splits >= p5b.splits_big);
+  // two verify blocks of 15 and 15 (bound 16): at least 14 tokens each -> only the big tile
+  pa_dims v2 = dims(2, 30, 16, 32, 8, 128, 64, 100, 16);
+  pa::Plan pv2 = pa::make_plan(&v2, PA_BF16, 256);
+  CHECK(!pv2.prefill && !pv2.dec_small && pv2.dec_big && pv2.big_nt == 4);
+  // a 5-token verify bound: 20 rows -> 32-row tile; 17 tokens over 4
+  // sequences leave room for one of 2 tokens (16-row tile)
+  pa_dims v5 = dims(4, 17, 5, 32, 8, 128, 64, 100, 16);
   pa::Plan pv = pa::make_plan(&v5, PA_BF16, 256);
   CHECK(!pv.prefill && pv.dec_small && pv.dec_big && pv.big_nt == 2);
+  v5.num_tokens = 20;                                      // four blocks of exactly 5
+  pv = pa::make_plan(&v5, PA_BF16, 256);
+  CHECK(!pv.prefill && !pv.dec_small && pv.dec_big && pv.big_nt == 2);
   // group 32: even one token needs 32 rows; decode class stops at 2 tokens
   pa_dims g32 = dims(2, 2, 1, 64, 2, 128, 64, 100, 16);
   pa::Plan pg = pa::make_plan(&g32, PA_BF16, 256);
