@@ -9,9 +9,14 @@
 //
 // The tile walks the sequence's pages in 64-key blocks and stops at the key
 // its last token can see (page "32. Production attention kernels": the key
-// loop stops at the tile's last query).  Blocks pass through a two-stage LDS
-// ring; each thread also holds up to PF further blocks in registers, so a
-// block's global loads are issued PF block-computes before they are needed.
+// loop stops at the tile's last query).  With bf16 pools and 128-dim heads
+// the blocks go from global memory straight into LDS (global_load_lds, no
+// register staging, no LDS stores) through a four-stage ring, three blocks
+// ahead of the one being computed; rows are 256 bytes with their 16-byte
+// chunks XOR-swizzled by key so the fragment reads stay conflict free.
+// Otherwise blocks pass through a two-stage ring of padded rows, and each
+// thread holds up to PF further blocks in registers (quantized pools are
+// dequantized on the way).
 // Per block and wave:
 //   S^T[64 keys x 32 rows] = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS);
 //   mask only blocks that reach the diagonal or the context end (page
@@ -95,7 +100,11 @@ template <int D, int NW, int PF, int KB, bool WIN, int KQ, bool CAS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void prefill_kernel(const AttnParams p) {
   using C = PrefillCfg<D, NW, PF, KB>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  // direct global -> LDS staging (see above)
+  constexpr bool DMA = KQ == KV_BF16 && D == 128;
+  constexpr int ROWB = D * 2, BLKB = KB * ROWB, DSTAGE = 2 * BLKB, DNS = 4;
+  constexpr int LDS_BYTES = DMA ? DNS * DSTAGE : C::LDS;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   int b, g, qt, split = 0;
   if constexpr (CAS) {
@@ -288,7 +297,28 @@ void prefill_kernel(const AttnParams p) {
   // S^T = K . Q^T for the 32-key tiles of block blk (raw scores)
   auto qk = [&](int blk, f32x16 (&st)[C::KT]) {
     const PA_LDS char* kl_ = lds + (blk % C::NSTAGE) * C::STAGE;
-    if constexpr (C::KT * C::DS <= 16) {
+    if constexpr (DMA) {
+      // key row k holds global chunk c at position c ^ (k & 15)
+      const PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
+      bf16x8 ka[C::KT][C::DS];
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          const int key = 32 * kt + l32;
+          ka[kt][s] = *(const PA_LDS bf16x8*)(kd + key * ROWB + 16 * ((2 * s + h2) ^ (key & 15)));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt) {
+        f32x16 a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) a = mfma32(ka[kt][s], qB[s], a);
+        st[kt] = a;
+      }
+    } else if constexpr (C::KT * C::DS <= 16) {
       // every K fragment of the block is requested before the first MFMA, so
       // the LDS latency is paid once per block rather than once per pair
       bf16x8 ka[C::KT][C::DS];
@@ -382,8 +412,19 @@ void prefill_kernel(const AttnParams p) {
             bf16x8, u32x4{pk[kt][4 * ks], pk[kt][4 * ks + 1], pk[kt][4 * ks + 2], pk[kt][4 * ks + 3]});
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const u32x2 a1 = lds_read_tr16(vr + kbase * C::VRS + 64 * dt);
-          const u32x2 a2 = lds_read_tr16(vr + (kbase + 8) * C::VRS + 64 * dt);
+          u32x2 a1, a2;
+          if constexpr (DMA) {
+            // value row k holds global chunk c at position c ^ 4 (k & 3): the
+            // four rows of a 16-lane transpose read land on distinct banks
+            const PA_LDS char* vd = lds + (blk % DNS) * DSTAGE + BLKB;
+            const int vk = 4 * h2 + (l16 >> 2), cb = 2 * (gq & 1) + ((l16 & 3) >> 1), sub = 8 * (l16 & 1);
+            const int k1 = kbase + vk, k2 = kbase + 8 + vk;
+            a1 = lds_read_tr16(vd + k1 * ROWB + 16 * ((4 * dt + cb) ^ (4 * (k1 & 3))) + sub);
+            a2 = lds_read_tr16(vd + k2 * ROWB + 16 * ((4 * dt + cb) ^ (4 * (k2 & 3))) + sub);
+          } else {
+            a1 = lds_read_tr16(vr + kbase * C::VRS + 64 * dt);
+            a2 = lds_read_tr16(vr + (kbase + 8) * C::VRS + 64 * dt);
+          }
           const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a1.x, a1.y, a2.x, a2.y});
           acc[dt] = mfma32(va, pb, acc[dt]);
         }
@@ -394,6 +435,82 @@ void prefill_kernel(const AttnParams p) {
   // registers hold blocks blk+1 .. blk+PF, issued PF blocks ahead.
   f32x16 st[C::KT];
   uint32_t pk[C::KT][8];
+  if constexpr (DMA) {
+    // Instruction i of wave w fills LDS bytes [(NW i + w) KiB, +1 KiB) of a
+    // K or V block: keys 4 (NW i + w) .. +3, lane l writing position l % 16 of
+    // key 4 (NW i + w) + l / 16.  Every lane of every wave issues every load,
+    // so all waves have the same count in flight: a key outside [lo, L)
+    // (lo: the first key any row of the tile uses) loads the nearest key
+    // inside, a finite copy of a live row whose score is masked and whose
+    // probability is 0.
+    constexpr int DL = BLKB / (C::NTH * 16);        // loads per thread per tensor
+    const int lkey = lane >> 4, lpos = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lo = wlo_tile;
+    // the lane's part of an address never changes: its key within a 4-key
+    // group (which never straddles a page) and its swizzled chunk
+    const int64_t lofs = (int64_t)lkey * p.kv_stride_slot;
+    const uint32_t lk = (uint32_t)((lofs + 8 * (lpos ^ ((4 * wv + lkey) & 15))) * 2);   // bytes
+    const uint32_t lv = (uint32_t)((lofs + 8 * (lpos ^ (4 * lkey))) * 2);
+    // page ids through the constant address space: scalar loads, which wait
+    // on their own counter rather than on the block loads in flight
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.table_width);
+    auto dma = [&](int blk) {
+      PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
+      if (blk * C::KB >= lo && blk * C::KB + C::KB <= L) {
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          const int kw = blk * C::KB + 4 * (NW * i + wv);
+          const int lp = kw >> psh;
+          const int pg = clampi(bt[lp], 0, p.num_pages - 1);
+          const int64_t row = ((int64_t)pg * p.kv_stride_page + (int64_t)(kw - (lp << psh)) * p.kv_stride_slot) * 2;
+          __builtin_amdgcn_global_load_lds((const void*)((const char*)kbase + row + lk),
+                                           (PA_LDS void*)(kd + (NW * i + wv) * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)((const char*)vbase + row + lv),
+                                           (PA_LDS void*)(kd + BLKB + (NW * i + wv) * 1024), 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          const int kw = blk * C::KB + 4 * (NW * i + wv);
+          const int jw = clampi(kw, lo, L - 1);
+          const int j = clampi(kw + lkey, lo, L - 1);
+          const int key = 4 * (NW * i + wv) + lkey;
+          // j and jw share a 4-key group (or are equal), hence a page
+          const int lp = jw >> psh;
+          const int pg = clampi(bt[lp], 0, p.num_pages - 1);
+          const int64_t row = (int64_t)pg * p.kv_stride_page + (int64_t)(j - (lp << psh)) * p.kv_stride_slot;
+          __builtin_amdgcn_global_load_lds((const void*)(kbase + row + 8 * (lpos ^ (key & 15))),
+                                           (PA_LDS void*)(kd + (NW * i + wv) * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(vbase + row + 8 * (lpos ^ (4 * (key & 3)))),
+                                           (PA_LDS void*)(kd + BLKB + (NW * i + wv) * 1024), 16, 0, 0);
+        }
+      }
+    };
+    // wait until at most `more` blocks (2 DL loads per thread each) issued
+    // after the one needed next are still in flight
+    auto wait_more = [&](int more) {
+      if (more >= 3) __builtin_amdgcn_s_waitcnt(0x3f70 | (6 * DL));         // vmcnt(6 DL)
+      else if (more == 2) __builtin_amdgcn_s_waitcnt(0x3f70 | (4 * DL));    // vmcnt(4 DL)
+      else if (more == 1) __builtin_amdgcn_s_waitcnt(0x3f70 | (2 * DL));    // vmcnt(2 DL)
+      else __builtin_amdgcn_s_waitcnt(0x3f70);                              // vmcnt(0)
+    };
+    static_assert(DNS == 4 && 6 * DL < 16, "wait_more counts up to three blocks");
+#pragma unroll
+    for (int x = 0; x < DNS; ++x)
+      if (blk0 + x < nblk) dma(blk0 + x);
+    wait_more(min(DNS - 1, nblk - 1 - blk0));       // block blk0 landed
+    __syncthreads();
+    for (int blk = blk0; blk < nblk; ++blk) {
+      qk(blk, st);
+      softmax(blk, st, pk);
+      pv(blk, pk);
+      wait_more(min(DNS - 2, nblk - 1 - (blk + 1)));   // block blk+1 landed
+      __syncthreads();
+      if (blk + DNS < nblk) dma(blk + DNS);            // into the stage block blk left
+    }
+  } else {
   PrefillRegs<D, NW, KB, KQ> rg[PF];
   if (blk0 < nblk) {
     gload(blk0, rg[0]);
@@ -416,6 +533,7 @@ void prefill_kernel(const AttnParams p) {
         if (blk + 1 + PF < nblk) gload(blk + 1 + PF, rg[k]);
       }
     }
+  }
   }
 
   // ---- normalise and write this lane's row (dims 32*dt + 8*(r/4) + 4*h2 + r%4)
