@@ -300,6 +300,11 @@ void prefill_kernel(const AttnParams p) {
     if constexpr (DMA) {
       // key row k holds global chunk c at position c ^ (k & 15)
       const PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
+      // the first tile's fragments are requested up front; the second tile's
+      // are requested one per MFMA of the first, so the first MFMA waits for
+      // one read and no more than 15 reads are ever in flight (the counter's
+      // range)
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 ka[C::KT][C::DS];
 #pragma unroll
       for (int kt = 0; kt < C::KT; ++kt)
@@ -308,7 +313,6 @@ void prefill_kernel(const AttnParams p) {
           const int key = 32 * kt + l32;
           ka[kt][s] = *(const PA_LDS bf16x8*)(kd + key * ROWB + 16 * ((2 * s + h2) ^ (key & 15)));
         }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kt = 0; kt < C::KT; ++kt) {
         f32x16 a;
@@ -318,6 +322,15 @@ void prefill_kernel(const AttnParams p) {
         for (int s = 0; s < C::DS; ++s) a = mfma32(ka[kt][s], qB[s], a);
         st[kt] = a;
       }
+      static_assert(C::KT == 2 && C::DS == 8, "read/MFMA interleave written for two 32-key tiles of 8 k-steps");
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // 8 LDS reads (tile 0)
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA (tile 0)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read (tile 1)
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMA (tile 1)
+      __builtin_amdgcn_sched_barrier(0);
     } else if constexpr (C::KT * C::DS <= 16) {
       // every K fragment of the block is requested before the first MFMA, so
       // the LDS latency is paid once per block rather than once per pair
@@ -367,11 +380,18 @@ void prefill_kernel(const AttnParams p) {
           st[kt][r] = vis ? st[kt][r] : kNegInf;
         }
     }
-    float bmax = kNegInf;
+    // one max3 per two scores, one chain per 32-key tile
+    float tm[C::KT];
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
+    for (int kt = 0; kt < C::KT; ++kt) {
+      float m = st[kt][0];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) bmax = fmaxf(bmax, fmaxf(st[kt][r], st[kt][r + 1]));
+      for (int r = 1; r < 15; r += 2) m = fmaxf(fmaxf(m, st[kt][r]), st[kt][r + 1]);
+      tm[kt] = fmaxf(m, st[kt][15]);
+    }
+    float bmax = tm[0];
+#pragma unroll
+    for (int kt = 1; kt < C::KT; ++kt) bmax = fmaxf(bmax, tm[kt]);
     bmax = xor32_max(bmax);
     const float m_blk = bmax * c;               // -inf stays -inf (c > 0)
     // lazy rescale: move the reference max only when this block exceeds it by > TAU
