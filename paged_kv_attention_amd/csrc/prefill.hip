@@ -57,6 +57,10 @@
 
 namespace pa {
 
+// s_waitcnt immediate (gfx9 layout) that waits until at most n vector-memory
+// operations are in flight and does not wait on the other counters
+constexpr int vm_wait(int n) { return 0x3f70 | (n & 0xf) | ((n >> 4) << 14); }
+
 template <int D, int NW, int PF, int KB_ = 64>
 struct PrefillCfg {
   static constexpr int NTH = 64 * NW;            // threads per workgroup
@@ -101,8 +105,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
 void prefill_kernel(const AttnParams p) {
   using C = PrefillCfg<D, NW, PF, KB>;
   // direct global -> LDS staging (see above)
-  constexpr bool DMA = KQ == KV_BF16 && D == 128;
-  constexpr int ROWB = D * 2, BLKB = KB * ROWB, DSTAGE = 2 * BLKB, DNS = 4;
+  constexpr bool DMA = KQ == KV_BF16 && (D == 128 || D == 256);
+  constexpr int ROWB = D * 2, BLKB = KB * ROWB, DSTAGE = 2 * BLKB, DNS = D == 128 ? 4 : 2;
+  constexpr int KPI = 1024 / ROWB;               // keys per 1 KiB DMA instruction
+  constexpr int CPR = ROWB / 16;                 // 16-byte chunks per key row
   constexpr int LDS_BYTES = DMA ? DNS * DSTAGE : C::LDS;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -297,7 +303,24 @@ void prefill_kernel(const AttnParams p) {
   // S^T = K . Q^T for the 32-key tiles of block blk (raw scores)
   auto qk = [&](int blk, f32x16 (&st)[C::KT]) {
     const PA_LDS char* kl_ = lds + (blk % C::NSTAGE) * C::STAGE;
-    if constexpr (DMA) {
+    if constexpr (DMA && C::DS > 8) {
+      // key row k holds global chunk c at position c ^ (k & 15); 256-dim
+      // rows: fragments read just before their MFMA
+      const PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt) {
+        f32x16 a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = 0.f;
+        const int key = 32 * kt + l32;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          const bf16x8 ka = *(const PA_LDS bf16x8*)(kd + key * ROWB + 16 * ((2 * s + h2) ^ (key & 15)));
+          a = mfma32(ka, qB[s], a);
+        }
+        st[kt] = a;
+      }
+    } else if constexpr (DMA) {
       // key row k holds global chunk c at position c ^ (k & 15)
       const PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
       // the first tile's fragments are requested up front; the second tile's
@@ -457,21 +480,26 @@ void prefill_kernel(const AttnParams p) {
   uint32_t pk[C::KT][8];
   if constexpr (DMA) {
     // Instruction i of wave w fills LDS bytes [(NW i + w) KiB, +1 KiB) of a
-    // K or V block: keys 4 (NW i + w) .. +3, lane l writing position l % 16 of
-    // key 4 (NW i + w) + l / 16.  Every lane of every wave issues every load,
-    // so all waves have the same count in flight: a key outside [lo, L)
-    // (lo: the first key any row of the tile uses) loads the nearest key
-    // inside, a finite copy of a live row whose score is masked and whose
-    // probability is 0.
+    // K or V block: keys KPI (NW i + w) .. +KPI-1, lane l writing position
+    // l % CPR of key KPI (NW i + w) + l / CPR.  Every lane of every wave
+    // issues every load, so all waves have the same count in flight: a key
+    // outside [lo, L) (lo: the first key any row of the tile uses) loads the
+    // nearest key inside, a finite copy of a live row whose score is masked
+    // and whose probability is 0.
     constexpr int DL = BLKB / (C::NTH * 16);        // loads per thread per tensor
-    const int lkey = lane >> 4, lpos = lane & 15;
+    const int lkey = lane / CPR, lpos = lane % CPR;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int lo = wlo_tile;
-    // the lane's part of an address never changes: its key within a 4-key
-    // group (which never straddles a page) and its swizzled chunk
+    // the lane's part of an address: its key within a KPI-key group (which
+    // never straddles a page) and its swizzled chunk; with 256-byte rows it
+    // is the same for every instruction, with 512-byte rows it alternates
     const int64_t lofs = (int64_t)lkey * p.kv_stride_slot;
-    const uint32_t lk = (uint32_t)((lofs + 8 * (lpos ^ ((4 * wv + lkey) & 15))) * 2);   // bytes
-    const uint32_t lv = (uint32_t)((lofs + 8 * (lpos ^ (4 * lkey))) * 2);
+    auto lane_k = [&](int i) {
+      return (uint32_t)((lofs + 8 * (lpos ^ ((KPI * (NW * i + wv) + lkey) & 15))) * 2);   // bytes
+    };
+    auto lane_v = [&](int i) {
+      return (uint32_t)((lofs + 8 * (lpos ^ (4 * ((KPI * (NW * i + wv) + lkey) & 3)))) * 2);
+    };
     // page ids through the constant address space: scalar loads, which wait
     // on their own counter rather than on the block loads in flight
     const __attribute__((address_space(4))) int32_t* bt =
@@ -481,23 +509,23 @@ void prefill_kernel(const AttnParams p) {
       if (blk * C::KB >= lo && blk * C::KB + C::KB <= L) {
 #pragma unroll
         for (int i = 0; i < DL; ++i) {
-          const int kw = blk * C::KB + 4 * (NW * i + wv);
+          const int kw = blk * C::KB + KPI * (NW * i + wv);
           const int lp = kw >> psh;
           const int pg = clampi(bt[lp], 0, p.num_pages - 1);
           const int64_t row = ((int64_t)pg * p.kv_stride_page + (int64_t)(kw - (lp << psh)) * p.kv_stride_slot) * 2;
-          __builtin_amdgcn_global_load_lds((const void*)((const char*)kbase + row + lk),
+          __builtin_amdgcn_global_load_lds((const void*)((const char*)kbase + row + lane_k(i)),
                                            (PA_LDS void*)(kd + (NW * i + wv) * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const void*)((const char*)vbase + row + lv),
+          __builtin_amdgcn_global_load_lds((const void*)((const char*)vbase + row + lane_v(i)),
                                            (PA_LDS void*)(kd + BLKB + (NW * i + wv) * 1024), 16, 0, 0);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < DL; ++i) {
-          const int kw = blk * C::KB + 4 * (NW * i + wv);
+          const int kw = blk * C::KB + KPI * (NW * i + wv);
           const int jw = clampi(kw, lo, L - 1);
           const int j = clampi(kw + lkey, lo, L - 1);
-          const int key = 4 * (NW * i + wv) + lkey;
-          // j and jw share a 4-key group (or are equal), hence a page
+          const int key = KPI * (NW * i + wv) + lkey;
+          // j and jw share a KPI-key group (or are equal), hence a page
           const int lp = jw >> psh;
           const int pg = clampi(bt[lp], 0, p.num_pages - 1);
           const int64_t row = (int64_t)pg * p.kv_stride_page + (int64_t)(j - (lp << psh)) * p.kv_stride_slot;
@@ -511,12 +539,12 @@ void prefill_kernel(const AttnParams p) {
     // wait until at most `more` blocks (2 DL loads per thread each) issued
     // after the one needed next are still in flight
     auto wait_more = [&](int more) {
-      if (more >= 3) __builtin_amdgcn_s_waitcnt(0x3f70 | (6 * DL));         // vmcnt(6 DL)
-      else if (more == 2) __builtin_amdgcn_s_waitcnt(0x3f70 | (4 * DL));    // vmcnt(4 DL)
-      else if (more == 1) __builtin_amdgcn_s_waitcnt(0x3f70 | (2 * DL));    // vmcnt(2 DL)
-      else __builtin_amdgcn_s_waitcnt(0x3f70);                              // vmcnt(0)
+      if (more >= 3) __builtin_amdgcn_s_waitcnt(vm_wait(6 * DL));
+      else if (more == 2) __builtin_amdgcn_s_waitcnt(vm_wait(4 * DL));
+      else if (more == 1) __builtin_amdgcn_s_waitcnt(vm_wait(2 * DL));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(0));
     };
-    static_assert(DNS == 4 && 6 * DL < 16, "wait_more counts up to three blocks");
+    static_assert(DNS >= 2 && DNS <= 4 && 2 * (DNS - 1) * DL < 64, "wait_more counts up to three blocks");
 #pragma unroll
     for (int x = 0; x < DNS; ++x)
       if (blk0 + x < nblk) dma(blk0 + x);
