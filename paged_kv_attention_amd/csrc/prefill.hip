@@ -506,7 +506,21 @@ void prefill_kernel(const AttnParams p) {
         (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.table_width);
     auto dma = [&](int blk) {
       PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
-      if (blk * C::KB >= lo && blk * C::KB + C::KB <= L) {
+      if (blk * C::KB >= lo && blk * C::KB + C::KB <= L && ps >= C::KB) {
+        // the whole block lies in one page: one page id for all its loads
+        const int kb = blk * C::KB;
+        const int lp = kb >> psh;
+        const int pg = clampi(bt[lp], 0, p.num_pages - 1);
+        const int64_t base = (int64_t)pg * p.kv_stride_page + (int64_t)(kb - (lp << psh)) * p.kv_stride_slot;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          const int64_t row = (base + (int64_t)(KPI * (NW * i + wv)) * p.kv_stride_slot) * 2;   // bytes
+          __builtin_amdgcn_global_load_lds((const void*)((const char*)kbase + row + lane_k(i)),
+                                           (PA_LDS void*)(kd + (NW * i + wv) * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)((const char*)vbase + row + lane_v(i)),
+                                           (PA_LDS void*)(kd + BLKB + (NW * i + wv) * 1024), 16, 0, 0);
+        }
+      } else if (blk * C::KB >= lo && blk * C::KB + C::KB <= L) {
 #pragma unroll
         for (int i = 0; i < DL; ++i) {
           const int kw = blk * C::KB + KPI * (NW * i + wv);
