@@ -504,13 +504,15 @@ void prefill_kernel(const AttnParams p) {
     // on their own counter rather than on the block loads in flight
     const __attribute__((address_space(4))) int32_t* bt =
         (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.table_width);
-    auto dma = [&](int blk) {
+    // raw page id of a whole-page block, fetched a block-compute ahead
+    auto page_raw = [&](int blk) { return bt[min((blk * C::KB) >> psh, p.table_width - 1)]; };
+    auto dma = [&](int blk, int pgraw) {
       PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
       if (blk * C::KB >= lo && blk * C::KB + C::KB <= L && ps >= C::KB) {
         // the whole block lies in one page: one page id for all its loads
         const int kb = blk * C::KB;
         const int lp = kb >> psh;
-        const int pg = clampi(bt[lp], 0, p.num_pages - 1);
+        const int pg = clampi(pgraw, 0, p.num_pages - 1);
         const int64_t base = (int64_t)pg * p.kv_stride_page + (int64_t)(kb - (lp << psh)) * p.kv_stride_slot;
 #pragma unroll
         for (int i = 0; i < DL; ++i) {
@@ -561,16 +563,17 @@ void prefill_kernel(const AttnParams p) {
     static_assert(DNS >= 2 && DNS <= 4 && 2 * (DNS - 1) * DL < 64, "wait_more counts up to three blocks");
 #pragma unroll
     for (int x = 0; x < DNS; ++x)
-      if (blk0 + x < nblk) dma(blk0 + x);
+      if (blk0 + x < nblk) dma(blk0 + x, page_raw(blk0 + x));
     wait_more(min(DNS - 1, nblk - 1 - blk0));       // block blk0 landed
     __syncthreads();
     for (int blk = blk0; blk < nblk; ++blk) {
+      const int pnext = page_raw(blk + DNS);          // in flight while the block computes
       qk(blk, st);
       softmax(blk, st, pk);
       pv(blk, pk);
       wait_more(min(DNS - 2, nblk - 1 - (blk + 1)));   // block blk+1 landed
       __syncthreads();
-      if (blk + DNS < nblk) dma(blk + DNS);            // into the stage block blk left
+      if (blk + DNS < nblk) dma(blk + DNS, pnext);     // into the stage block blk left
     }
   } else {
   PrefillRegs<D, NW, KB, KQ> rg[PF];
