@@ -94,7 +94,10 @@ def test_bf16_group3_and_mha():
 
 
 # ---------------------------------------------------------------- bf16 prefill
-@pytest.mark.parametrize("D,ps", [(128, 64), (64, 16), (256, 32), (128, 128)])
+# (128, 16/32) and (256, 32): blocks span several pages (one page id per
+# 4- or 2-key group); (128, 64/128) and (256, 64/128): one page per block
+@pytest.mark.parametrize("D,ps", [(128, 64), (64, 16), (256, 32), (128, 128), (128, 16), (128, 32), (256, 64),
+                                  (256, 128)])
 def test_bf16_prefill(D, ps):
     lens = [300, 700, 129]
     qlens = [300, 200, 17]

@@ -59,7 +59,8 @@ def test_bf16_verify_window_sinks(qlens):
         check(w, got, window=window, sinks=sk, label=f"verify {qlens} window {window}")
 
 
-@pytest.mark.parametrize("D,ps,causal", [(128, 64, True), (64, 16, True), (256, 32, True), (128, 64, False)])
+@pytest.mark.parametrize("D,ps,causal", [(128, 64, True), (64, 16, True), (256, 32, True), (128, 64, False),
+                                           (128, 16, True), (256, 128, True)])
 @pytest.mark.parametrize("window", [100, 300, 1023])
 def test_bf16_prefill_window_sinks(D, ps, causal, window):
     Hq, Hkv = (16, 4) if D == 256 else (8, 2)
