@@ -431,8 +431,44 @@ def _time_steps(step_fns, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
-    per = [sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)) / steps for j in range(len(step_fns))]
+    times = [[evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)] for j in range(len(step_fns))]
+    per = [sum(t) / steps for t in times]
+    _time_steps.last = times
     return total, per
+
+
+def _spread(times):
+    """Median and minimum of one function's per-step times (ms)."""
+    t = sorted(times)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return {"median": round(med, 5), "min": round(t[0], 5)}
+
+
+def read_ceiling(reps=10):
+    """HBM streaming-read rate of the library's read probe (16-byte
+    nontemporal loads over a 4 GiB buffer, best of `reps`): the practical
+    ceiling for a kernel that streams K/V pages, which the decode kernel's
+    read rate is compared with."""
+    import torch
+    import paged_kv_attention_amd as pa
+    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    sink = torch.empty(pa.READ_PROBE_SINK_BYTES, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        pa.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        e0.record()
+        pa.read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return round(4 * (1 << 30) / (best * 1e-3) / 1e9, 1)
 
 
 def cpu_baseline(w, seconds_target=12.0):
@@ -509,6 +545,7 @@ def main():
         ms = total / args.steps
         value = db.attn_bytes / (ms * 1e-3) / 1e9
         kern_ms = per[1]
+        kern_spread = _spread(_time_steps.last[1])
         achieved = db.attn_bytes / (kern_ms * 1e-3) / 1e9
         traffic = measured_traffic("decode")
         result.update({
@@ -524,6 +561,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "kernel": "decode_splitkv_kernel<128,1>", "kernel_ms": round(kern_ms, 5),
+                         "kernel_ms_median": kern_spread["median"], "kernel_ms_min": kern_spread["min"],
                          "bytes_per_launch": db.attn_bytes},
             "kv_write_ms": round(per[0], 5),
         })
@@ -535,6 +573,11 @@ def main():
         decode_w = db.w
         del db
         torch.cuda.empty_cache()
+        if args.only is None:
+            ceil = read_ceiling()
+            result["read_ceiling"] = {"GB_s": ceil, "decode_frac": round(achieved / ceil, 4),
+                                      "how": "library read probe (pa_read_probe): 16-byte streaming loads "
+                                             "over a 4 GiB buffer, best of 10"}
 
     if args.only in (None, "prefill") and not args.no_prefill:
         print("[bench] prefill: building inputs", file=sys.stderr, flush=True)
@@ -542,6 +585,7 @@ def main():
         psteps = max(3, min(args.steps, 10))
         total, per = _time_steps([lambda i: pb.write(), lambda i: pb.attend()], psteps, max(1, min(args.warmup, 3)))
         kern_ms = per[1]
+        kern_spread = _spread(_time_steps.last[1])
         step_ms = total / psteps
         tflops_kernel = pb.flops / (kern_ms * 1e-3) / 1e12
         tflops_step = pb.flops / (step_ms * 1e-3) / 1e12
@@ -552,7 +596,8 @@ def main():
                "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops_kernel / BF16_PEAK_TFLOPS, 4),
                             "traffic": measured_traffic("prefill"), "kernel": "prefill_kernel<128>",
-                            "kernel_ms": round(kern_ms, 4)}}
+                            "kernel_ms": round(kern_ms, 4), "kernel_ms_median": kern_spread["median"],
+                            "kernel_ms_min": kern_spread["min"]}}
         if args.only == "prefill":
             result.update({"metric": METRIC, "value": round(tflops_kernel, 2), "unit": "TFLOP/s", "n_gpus": 1,
                            "steps": psteps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),

@@ -298,6 +298,20 @@ const char* pa_status_string(pa_status status);
 /* pa_device_cu_count -- compute units of the current device (cached). */
 int32_t pa_device_cu_count(void);
 
+/*
+ * pa_read_probe -- measurement aid, not part of the attention path: reads the
+ * device buffer `buf` of `bytes` bytes once with 16-byte streaming loads
+ * (16384 workgroups of 256 threads) and writes one folded word per workgroup
+ * to the device buffer `sink`, so the reads cannot be elided.  The time it
+ * takes gives the HBM read rate a streaming kernel reaches on this device,
+ * the practical ceiling the decode kernel's read rate is compared with.
+ * `buf` must be 16-byte aligned and `bytes` a multiple of 16
+ * (PA_ERR_SHAPE otherwise); `sink` needs 65536 bytes (PA_ERR_WORKSPACE);
+ * NULL pointers give PA_ERR_NULL.  Asynchronous on `stream`; the caller owns
+ * both buffers.
+ */
+pa_status pa_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

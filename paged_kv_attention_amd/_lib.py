@@ -22,7 +22,7 @@ PA_F32, PA_BF16 = 0, 1
 
 EXPORTED = ("paged_attention", "paged_attention_opts", "kv_cache_write", "kv_cache_write_quant", "pa_workspace_size",
             "pa_workspace_size_opts", "pa_choose_splits", "pa_validate", "pa_validate_opts", "pa_status_string",
-            "pa_device_cu_count")
+            "pa_device_cu_count", "pa_read_probe")
 
 
 class PaDims(ctypes.Structure):
@@ -147,6 +147,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_device_cu_count.restype = ctypes.c_int32
     lib.pa_device_cu_count.argtypes = []
+    lib.pa_read_probe.restype = ctypes.c_int
+    lib.pa_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -299,6 +301,21 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if st != PA_OK:
         raise PagedAttnError(st, "paged_attention")
     return out
+
+
+READ_PROBE_SINK_BYTES = 65536
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream ``buf`` (a contiguous device tensor) once through the library's
+    read probe; ``sink`` is a device tensor of at least 65536 bytes.  A
+    measurement aid for the HBM read ceiling, not part of attention."""
+    if not buf.is_contiguous() or not sink.is_contiguous():
+        raise ValueError("buf and sink must be contiguous")
+    st = load_library().pa_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                      sink.numel() * sink.element_size(), _stream_ptr(stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_read_probe")
 
 
 def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -15,8 +15,10 @@
 //                                   (8 contiguous dims per lane);
 //   mask (only chunks that reach the causal diagonal or the split's end);
 //   m' = max(m, rowmax), alpha = exp2(m - m'), p = exp2(s - m') in float32;
-//   O^T[D x rows] += V^T . P^T      V staged through the wave's LDS tile and
-//                                   read back transposed (ds_read_b64_tr_b16);
+//   O^T[D x rows] += V^T . P^T      V loaded in whole rows with streaming
+//                                   (nontemporal) loads, staged through the
+//                                   wave's LDS tile and read back transposed
+//                                   (ds_read_b64_tr_b16);
 //                                   P^T is already in the B-operand layout of
 //                                   S^T's accumulator registers.
 // Scores use exp2 with scale*log2(e) folded in (page "Attention kernels", One
@@ -224,7 +226,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const int kl = idx / C::CPL, cc = idx % C::CPL;
       const int t = (i * 64 / C::CPL) / 16;       // uniform per load
       const char* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) * C::EB + 16 * cc;
-      ch.v[i] = *(const u32x4*)vp;
+      // a wave's V load covers whole rows (full cache lines) that no other
+      // workgroup reads: a streaming (nontemporal) load reads them faster
+      ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
     }
     if constexpr (QUANT) {
       // lane l: scale of key k0 + l % 32, of K for l < 32 and of V above;

@@ -113,3 +113,14 @@ def test_kv_write_argument_errors():
     assert lib.kv_cache_write(None, None, None, None, None, 4, 1024, 128, None, 1, None) == pa.PA_ERR_NULL
     assert lib.kv_cache_write(None, None, None, None, None, 4, 1024, 128, ctypes.byref(_dims(head_dim=80)), 1,
                               None) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_read_probe_rejects_bad_arguments_without_launch():
+    lib = pa.load_library()
+    sink = ctypes.c_void_p(4096)
+    assert lib.pa_read_probe(None, 16, sink, 65536, None) == pa.PA_ERR_NULL
+    assert lib.pa_read_probe(ctypes.c_void_p(4096), 16, None, 65536, None) == pa.PA_ERR_NULL
+    assert lib.pa_read_probe(ctypes.c_void_p(4096), 20, sink, 65536, None) == pa.PA_ERR_SHAPE      # not 16-byte sized
+    assert lib.pa_read_probe(ctypes.c_void_p(4104), 16, sink, 65536, None) == pa.PA_ERR_SHAPE      # not 16-byte aligned
+    assert lib.pa_read_probe(ctypes.c_void_p(4096), 16, sink, 1024, None) == pa.PA_ERR_WORKSPACE   # sink too small
+    assert lib.pa_read_probe(ctypes.c_void_p(4096), 0, sink, 65536, None) == pa.PA_OK              # nothing to read
