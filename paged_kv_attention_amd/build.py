@@ -90,5 +90,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_table(summary: str) -> str:
+    """One line per kernel instantiation: VGPRs, AGPRs, scratch bytes per
+    lane, LDS bytes per workgroup and waves per SIMD, from the remarks."""
+    rows, cur = [], None
+    for line in summary.splitlines():
+        m = re.match(r"\s*Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            rows.append(cur)
+            continue
+        m = re.match(r"\s*(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).split()[0]] = int(m.group(2))
+    out = [f"{'kernel (mangled)':90s} {'VGPR':>5s} {'AGPR':>5s} {'scratch':>7s} {'LDS':>7s} {'waves/SIMD':>10s}"]
+    for r in rows:
+        if not r["name"].startswith("_ZN2pa"):
+            continue
+        out.append(f"{r['name'][:90]:90s} {r.get('VGPRs', 0):5d} {r.get('AGPRs', 0):5d} {r.get('ScratchSize', 0):7d} "
+                   f"{r.get('LDS', 0):7d} {r.get('Occupancy', 0):10d}")
+    return "\n".join(out) + "\n"
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    lib = build(verbose="-v" in sys.argv)
+    if "--table" in sys.argv:
+        with open(os.path.join(BUILD, "resource_usage.txt")) as f:
+            print(resource_table(f.read()), end="")
+    else:
+        print(lib)
