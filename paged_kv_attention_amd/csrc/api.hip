@@ -317,6 +317,7 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
       return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
     if (pl.prefill) e = launch_prefill(p, s);
+    q1.head_first = classes == 1;            // decode tiles have the chip to themselves
     if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
     if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);

@@ -103,7 +103,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   constexpr int ORS = DecodeLds<D, NT, KQ>::ORS;
   __shared__ __attribute__((aligned(16))) char smem[DecodeLds<D, NT, KQ>::BYTES];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Grid order.  The hardware deals workgroups to the 8 XCDs in turn.  With
+  // the split fastest, split 0 (the longest) of every sequence lands on the
+  // same XCDs; a batch of decode tiles alone therefore runs with the KV head
+  // fastest, which gives each XCD the same heads of every sequence and split,
+  // an equal share of the work however ragged the sequences are.  Batches
+  // with prefill or verification tiles beside keep the split fastest, which
+  // measured faster there.
+  const bool hf = NT == 1 && p.head_first;
+  const int split = hf ? blockIdx.z : blockIdx.x;
+  const int g = hf ? blockIdx.x : blockIdx.y;
+  const int b = hf ? blockIdx.y : blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
 
@@ -503,7 +513,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 
 template <int D, int NT>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
-  dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
+  const dim3 grid = NT == 1 && p.head_first ? dim3(p.num_kv_heads, p.num_seqs, p.num_splits)
+                                            : dim3(p.num_splits, p.num_kv_heads, p.num_seqs);
   const bool win = p.window > 0 || p.key_lo > 0;
   switch (p.kv_code) {
     case KV_INT8:

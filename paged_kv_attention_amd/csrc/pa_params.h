@@ -62,6 +62,8 @@ struct AttnParams {
   int32_t prefix_split_keys;
   int32_t merge_prefix;     // decode with one split: fold this many prefix partials (slots 0..) into
                             // the output instead of writing a partial
+  int32_t head_first;       // 16-row decode tiles: grid (KV head, sequence, split) instead of
+                            // (split, KV head, sequence)
 };
 
 // First page of the split ranges of a sequence with context L and n step
