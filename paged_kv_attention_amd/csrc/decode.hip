@@ -95,7 +95,9 @@ struct DecodeChunk {
 
 // WIN: the launch has a sliding window (p.window > 0); KQ: the pools' code
 // type (KvCode).  The plain instantiation carries none of their code.
-template <int D, int NT, bool WIN, int KQ>
+// NB: register chunks per wave, 0 for the code type's default (see the main
+// loop).
+template <int D, int NT, bool WIN, int KQ, int NB = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D, KQ>;
   constexpr bool QUANT = KQ != KV_BF16;
@@ -394,17 +396,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   // while chunk c is computed.  NBUF = 1 (load a chunk, then compute it) is
   // the measured best on the 64 x 4096 decode step: a second chunk in flight
   // per wave (register double buffering, or issuing the next chunk's loads
-  // before this chunk's softmax) lowers the achieved HBM bandwidth.
-  DecodeChunk<D, KQ> buf[C::NBUF];
+  // before this chunk's softmax) lowers the achieved HBM bandwidth.  A launch
+  // with fewer workgroups than that (more than one split: the batch has too
+  // few (sequence, KV head) pairs to fill the chip, and its longest splits
+  // finish alone) keeps two chunks per wave in flight instead (NB = 2, for
+  // heads of up to 128 dims).
+  constexpr int NBUF = NB ? NB : C::NBUF;
+  DecodeChunk<D, KQ> buf[NBUF];
 #pragma unroll
-  for (int j = 0; j < C::NBUF - 1; ++j)
+  for (int j = 0; j < NBUF - 1; ++j)
     if (wave + 4 * j < nchunks) load(wave + 4 * j, buf[j]);
-  for (int base = wave; base < nchunks; base += 4 * C::NBUF) {
+  for (int base = wave; base < nchunks; base += 4 * NBUF) {
 #pragma unroll
-    for (int k = 0; k < C::NBUF; ++k) {
+    for (int k = 0; k < NBUF; ++k) {
       const int c = base + 4 * k;
-      const int cn = c + 4 * (C::NBUF - 1);
-      if (cn < nchunks) load(cn, buf[(k + C::NBUF - 1) % C::NBUF]);
+      const int cn = c + 4 * (NBUF - 1);
+      if (cn < nchunks) load(cn, buf[(k + NBUF - 1) % NBUF]);
       if (c < nchunks) process(c, buf[k]);
     }
   }
@@ -526,6 +533,15 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
       else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_FP8>), grid, dim3(256), 0, st, p);
       break;
     default:
+      // two chunks per wave in flight for split launches (see the main loop);
+      // 256-dim heads do not have the registers for it
+      if constexpr (NT == 1 && D <= 128) {
+        if (p.num_splits > 1) {
+          if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2>), grid, dim3(256), 0, st, p);
+          else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 2>), grid, dim3(256), 0, st, p);
+          break;
+        }
+      }
       if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16>), grid, dim3(256), 0, st, p);
       else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16>), grid, dim3(256), 0, st, p);
   }
