@@ -261,9 +261,10 @@ size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn
 /*
  * pa_choose_splits -- the split count paged_attention will use for decode
  * rows (one token, or n*G <= 16 rows): dims->num_splits when > 0, else enough
- * workgroups to fill every CU of the current device with at least 256 keys
- * per split and at most 32 splits (page "32. Production attention kernels",
- * How many splits?).  Verification blocks (16 < n*G <= 64 rows) use 8 splits
+ * workgroups for two per CU of the current device (three when every sequence
+ * has one token, max_query_len == 1, and two are not reached), with at least
+ * 256 keys per split and at most 32 splits (page "32. Production attention
+ * kernels", How many splits?).  Verification blocks (16 < n*G <= 64 rows) use 8 splits
  * unless dims->num_splits is set.  Returns 1 for invalid dims.
  */
 int32_t pa_choose_splits(const pa_dims* dims);

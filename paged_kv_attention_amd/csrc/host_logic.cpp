@@ -63,6 +63,11 @@ int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W) {
   int64_t target = dtype == PA_BF16 ? 2 * (int64_t)cu_count : 8 * (int64_t)cu_count;
   if (units < 1) units = 1;
   int64_t want = (target + units - 1) / units;
+  // A step of one-token decodes that cannot fill two workgroups per CU aims
+  // at three: it runs alone (no other tile class beside it), and more, shorter
+  // splits shorten the longest sequence's tail.  Mixed batches measured
+  // faster with two.
+  if (dtype == PA_BF16 && mql == 1 && units < target) want = (3 * (int64_t)cu_count + units - 1) / units;
   const int min_pages = (256 + d->page_size - 1) / d->page_size;
   const int64_t cap_pages = (W + min_pages - 1) / min_pages;
   int64_t s = want;

@@ -25,18 +25,22 @@ int main() {
   CHECK(pa::check_dims(&c3, PA_BF16) == PA_OK);
   pa::Plan p3 = pa::make_plan(&c3, PA_BF16, 256);
   CHECK(p3.splits == 1 && p3.workspace_bytes == 0 && p3.dec_small && !p3.dec_big && !p3.prefill && !p3.combine);
-  // ragged 32 sequences: two splits, workspace for every row
+  // ragged 32 one-token decodes: 256 (sequence, KV head) pairs do not fill
+  // two workgroups per CU, so three splits; workspace for every row
   pa_dims c2 = dims(32, 32, 1, 32, 8, 128, 64, 2000, 64);
   pa::Plan p2 = pa::make_plan(&c2, PA_BF16, 256);
-  CHECK(p2.splits == 2 && p2.pages_per_split == 32 && p2.combine && p2.comb_tokens == 1);
-  CHECK(p2.workspace_bytes == (size_t)2 * 32 * 32 * 130 * 4);
+  CHECK(p2.splits == 3 && p2.pages_per_split == 22 && p2.combine && p2.comb_tokens == 1);
+  CHECK(p2.workspace_bytes == (size_t)3 * 32 * 32 * 130 * 4);
+  // the same sequences with 2-token steps aim at two workgroups per CU
+  pa_dims c2v = dims(32, 64, 2, 32, 8, 128, 64, 2000, 64);
+  CHECK(pa::make_plan(&c2v, PA_BF16, 256).splits == 2);
   // sliding window: the splits cut the window's pages, never more than the table's
   CHECK(pa::window_pages(0, 1, 64, 64) == 64);
   CHECK(pa::window_pages(1024, 1, 64, 64) == 18);          // 1024 keys over at most 18 pages
   CHECK(pa::window_pages(100000, 1, 64, 64) == 64);
   CHECK(pa::window_pages(1, 16, 16, 64) == 3);          // 16 keys straddle at most 2 pages; one spare
   pa::Plan pw = pa::make_plan(&c2, PA_BF16, 256, 1024);
-  CHECK(pw.window == 1024 && pw.splits == 2 && pw.pages_per_split == 9);
+  CHECK(pw.window == 1024 && pw.splits == 3 && pw.pages_per_split == 6);
   CHECK(pw.workspace_bytes <= p2.workspace_bytes);
   // split ranges start at the page of the first token's window start
   CHECK(pa::split_page_base(4096, 1, 1024, 64) == 48 && pa::split_page_base(4096, 1, 0, 64) == 0);
