@@ -279,12 +279,17 @@ def other_workloads(steps, warmup):
                               (4, 8, "bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify")]:
         print(f"[bench] other workload {cfg}: building inputs", file=sys.stderr, flush=True)
         wb = WorkloadBench(cfg, layers)
-        total, per = _time_steps([wb.attend], steps, warmup)
+        _, per = _time_steps([wb.attend], steps, warmup)
         ms = per[0]
-        # calls back to back: events around all timed calls, so the host's
-        # launch path overlaps the GPU's work (the call-by-call figure above
-        # includes it when the host is slower than the call's kernels)
-        ms_b2b = total / steps
+        # calls back to back: two events around all calls and none between
+        # them, so the host's launch path runs ahead of the GPU's work
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            wb.attend(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_b2b = e0.elapsed_time(e1) / steps
         entry = {"workload": name, "ms": round(ms, 5), "ms_back_to_back": round(ms_b2b, 5), "splits": wb.splits,
                  "algorithmic_bytes": wb.bytes, "GB_s": round(wb.bytes / (ms * 1e-3) / 1e9, 2),
                  "hbm_frac": round(wb.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
