@@ -14,11 +14,16 @@
  *   allocates no memory, keeps no per-call state and never reads device
  *   memory back in paged_attention / kv_cache_write, so both can be captured
  *   in a hipGraph.  Cached per device: the CU count, and two side streams
- *   with three events (default priority), created by the first bf16 call
- *   outside graph capture that launches more than one tile class (16-row
- *   decode tiles, verification tiles, prefill tiles: decided on the host from
- *   max_query_len and the group size) and kept until the process ends.  A
- *   graph captured before they exist gets serial launches.
+ *   with three events (default priority), created by the first bf16
+ *   paged_attention call made outside graph capture and kept until the
+ *   process ends.  They serve calls that launch more than one tile class
+ *   (16-row decode tiles, verification tiles, prefill tiles: decided on the
+ *   host from max_query_len and the group size).  HIP deals streams to the
+ *   process's hardware queues in creation order, so making the first call
+ *   before creating other streams keeps the side streams on queues of their
+ *   own; side streams that share a queue with `stream` run their launches
+ *   one after another.  A graph captured before they exist gets serial
+ *   launches.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *   void*; NULL = the default stream).  Nothing is synchronised.  A mixed
  *   call forks into the side streams through an event recorded on `stream`
