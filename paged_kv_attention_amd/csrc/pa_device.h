@@ -88,12 +88,20 @@ __device__ __forceinline__ u32x2 i8x4_to_bf16_biased(uint32_t w) {
                pack_bf16x2((float)((u >> 16) & 0xffu), (float)(u >> 24))};
 }
 
-// 4 codes -> 4 bf16 (two packed words)
+// 4 codes -> 4 bf16 (two packed words).  Float8 E4M3 goes straight to bf16,
+// two codes per instruction (gfx950's scaled conversion with scale 1; every
+// E4M3 value is a bf16 value, so it is exact).
 template <int KQ>
 __device__ __forceinline__ u32x2 codes4_to_bf16(uint32_t w) {
-  float f[4];
-  codes4_to_f32<KQ>(w, f);
-  return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+  if constexpr (KQ == KV_FP8) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  } else {
+    float f[4];
+    codes4_to_f32<KQ>(w, f);
+    return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+  }
 }
 
 // Cross-lane helpers over the 64-lane wave.
