@@ -165,6 +165,14 @@ class DecodeBench:
         k, v = self.pools[layer % len(self.pools)]
         self.pa.kv_cache_write(self.k_new, self.v_new, k, v, self.slots)
 
+    def step(self, layer):
+        """The decode step as one call: the new rows go in with the attention
+        (the decode launch writes them before reading a key)."""
+        k, v = self.pools[layer % len(self.pools)]
+        return self.pa.paged_attention(self.q, k, v, self.bt, self.cl, self.qsl, self.w.scale, True, out=self.out,
+                                       workspace=self.ws, max_query_len=1, num_splits=self.num_splits,
+                                       k_new=self.k_new, v_new=self.v_new, slot_mapping=self.slots)
+
 
 
 class PrefillBench:
@@ -559,6 +567,7 @@ def main():
     if args.only in (None, "decode"):
         print("[bench] decode: building inputs", file=sys.stderr, flush=True)
         db = DecodeBench(layers=args.layers, num_splits=args.num_splits)
+        # the step: kv_cache_write of the 64 new rows, then paged_attention
         total, per = _time_steps([db.write, db.attend], args.steps, args.warmup)
         ms = total / args.steps
         value = db.attn_bytes / (ms * 1e-3) / 1e9
@@ -583,6 +592,15 @@ def main():
                          "bytes_per_launch": db.attn_bytes},
             "kv_write_ms": round(per[0], 5),
         })
+        if args.only is None:
+            # the same step as one call: paged_attention with the new rows,
+            # which its decode launch writes before reading a key
+            total2, per2 = _time_steps([db.step], args.steps, args.warmup)
+            result["one_call_step"] = {
+                "ms_per_step": round(total2 / args.steps, 5),
+                "GB_s": round(db.attn_bytes / (total2 / args.steps * 1e-3) / 1e9, 2),
+                "kernel_ms": round(per2[0], 5),
+                "note": "paged_attention(k_new, v_new, slot_mapping): one decode launch writes and attends"}
         if not args.no_graph:
             g_ms = graph_step(db, args.steps)
             result["graph_step"] = {"ms_per_step": round(g_ms, 5),

@@ -195,6 +195,21 @@ typedef struct pa_attn_opts {
   const pa_kv_quant* kv_quant;
   int32_t shared_prefix_len;
   int32_t reserved1;       /* must be 0 */
+  /* The step's new K/V rows: with k_new set, the call first writes them as
+   * kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping,
+   * dims->num_tokens, new_stride_tok, new_stride_head, dims, dtype) would,
+   * then attends; so the pools are written (plain pools only: with kv_quant,
+   * PA_ERR_UNSUPPORTED).  A batch of decode tokens alone (no prefill or
+   * verification tiles) does the write inside its decode launch: the
+   * workgroup whose pages hold a token's position writes that token's rows
+   * of its KV head before it reads a key, which requires every new token's
+   * slot to be the one its own sequence's table gives for its position (the
+   * contract of a decode step; pa_validate checks slots, not this).  Other
+   * batches launch the write first.  k_new == NULL: no write. */
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int64_t new_stride_tok, new_stride_head;   /* element strides of [N, Hkv, D] k_new / v_new */
 } pa_attn_opts;
 
 /*

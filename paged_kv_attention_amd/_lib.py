@@ -47,7 +47,9 @@ class PaKvQuant(ctypes.Structure):
 class PaAttnOpts(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("sinks", ctypes.c_void_p),
                 ("kv_quant", ctypes.POINTER(PaKvQuant)), ("shared_prefix_len", ctypes.c_int32),
-                ("reserved1", ctypes.c_int32)]
+                ("reserved1", ctypes.c_int32), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+                ("slot_mapping", ctypes.c_void_p), ("new_stride_tok", ctypes.c_int64),
+                ("new_stride_head", ctypes.c_int64)]
 
 
 PA_KV_INT8, PA_KV_FP8_E4M3 = 1, 2
@@ -244,7 +246,9 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                     causal: bool = True, *, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, max_query_len: Optional[int] = None,
                     num_splits: int = 0, window: int = 0, sinks: Optional[torch.Tensor] = None,
-                    kv_quant: Optional[KvQuant] = None, shared_prefix_len: int = 0, stream=None) -> torch.Tensor:
+                    kv_quant: Optional[KvQuant] = None, shared_prefix_len: int = 0,
+                    k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                    slot_mapping: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Causal GQA attention of q over the paged pools; returns ``out`` [N, Hq, D].
 
     ``scale`` defaults to 1/sqrt(D).  ``max_query_len`` is a host bound on any
@@ -255,6 +259,10 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     ``kv_quant`` the pools are 1-byte code pools (int8 / float8_e4m3fn) and
     q must be bfloat16.  ``shared_prefix_len`` > 0 runs cascade attention
     over a prefix every sequence shares (same first pages, queries after it).
+    ``k_new`` / ``v_new`` ([N, Hkv, D], q's dtype) with ``slot_mapping`` (int32
+    [N]) write the step's new rows into the pools before attending, as
+    ``kv_cache_write`` would; a batch of decode tokens alone does the write
+    inside its decode launch.
     """
     lib = load_library()
     if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
@@ -272,7 +280,19 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     qsl = _i32(query_start_loc, "query_start_loc")
     code = _dtype_code(q.dtype)
     opts = None
-    if window or sinks is not None or kv_quant is not None or shared_prefix_len:
+    if k_new is not None:
+        if v_new is None or slot_mapping is None:
+            raise ValueError("k_new needs v_new and slot_mapping")
+        if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dim() != 3:
+            raise ValueError("k_new and v_new must be [N, Hkv, D] with the same strides")
+        if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+            raise TypeError("new rows must have q's dtype")
+        if k_new.stride(2) != 1:
+            raise ValueError("the head dimension of the new rows must be contiguous")
+        if k_new.shape[0] != q.shape[0] or tuple(k_new.shape[1:]) != (k_pool.shape[2], k_pool.shape[3]):
+            raise ValueError("k_new must be [N, Hkv, D]: one new row per query token and KV head")
+        slot_mapping = _i32(slot_mapping, "slot_mapping")
+    if window or sinks is not None or kv_quant is not None or shared_prefix_len or k_new is not None:
         if sinks is not None:
             if sinks.dtype != torch.float32 or sinks.device != q.device or sinks.numel() != q.shape[1]:
                 raise ValueError("sinks must be a float32 tensor of num_q_heads values on q's device")
@@ -280,6 +300,9 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
         kq = kv_quant.struct() if kv_quant is not None else None
         opts = PaAttnOpts(int(window), 0, sinks.data_ptr() if sinks is not None else None,
                           ctypes.pointer(kq) if kq is not None else None, int(shared_prefix_len), 0)
+        if k_new is not None:
+            opts.k_new, opts.v_new, opts.slot_mapping = k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr()
+            opts.new_stride_tok, opts.new_stride_head = k_new.stride(0), k_new.stride(1)
         need = int(lib.pa_workspace_size_opts(ctypes.byref(dims), code, ctypes.byref(opts)))
     else:
         need = int(lib.pa_workspace_size(ctypes.byref(dims), code))

@@ -34,6 +34,7 @@ static int cu_count() {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Argument checks of a quantized-pool description (nothing is read from the
@@ -101,6 +102,10 @@ static SideStreams* lock_side_streams(hipStream_t caller) {
 using namespace pa;
 
 extern "C" {
+static pa_status kv_write_setup(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
+                                const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
+                                int64_t new_stride_head, const pa_dims* dims, pa_dtype dtype, KvWriteParams& p);
+
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -162,6 +167,14 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   if (kq) {
     if ((st = check_kv_quant(kq, dims)) != PA_OK) return st;
     if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  }
+  // the step's new rows, written before the call attends
+  KvWriteParams wp{};
+  if (opts && opts->k_new) {
+    if (kq) return PA_ERR_UNSUPPORTED;       // a quantizing write is kv_cache_write_quant's
+    if ((st = kv_write_setup(opts->k_new, opts->v_new, k_pool, v_pool, opts->slot_mapping, dims->num_tokens,
+                             opts->new_stride_tok, opts->new_stride_head, dims, dtype, wp)) != PA_OK)
+      return st;
   }
   if (dims->num_seqs == 0 || dims->num_tokens == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start_loc || !out) return PA_ERR_NULL;
@@ -270,14 +283,16 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
       q1.merge_prefix = q2.merge_prefix = cp.prefix_splits;
       q1.force_partial = q2.force_partial = 0;
     }
-    if (cp.prefix_splits > 0) e = launch_prefix(pre, s);
+    if (wp.num_tokens > 0) e = launch_kv_write(wp, s);
+    if (e == hipSuccess && cp.prefix_splits > 0) e = launch_prefix(pre, s);
     if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
     if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
     if (e == hipSuccess && !fold) e = launch_combine(p, true, s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   }
   if (dtype == PA_F32) {
-    e = launch_f32(p, pl.mql, s);
+    if (wp.num_tokens > 0) e = launch_kv_write(wp, s);
+    if (e == hipSuccess) e = launch_f32(p, pl.mql, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, false, s);
   } else {
     AttnParams q1 = p;                       // 16-row decode tiles
@@ -289,6 +304,11 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
     q2.num_splits = pl.splits_big;
     q2.pages_per_split = pl.pages_per_split_big;
     const int classes = (int)pl.prefill + (int)pl.dec_small + (int)pl.dec_big;
+    // New rows: a batch of 16-row decode tiles alone writes them inside its
+    // decode launch (each workgroup the rows of its own KV head and pages,
+    // before it reads a key); otherwise they are written first.
+    const bool fuse = wp.num_tokens > 0 && classes == 1 && pl.dec_small;
+    if (wp.num_tokens > 0 && !fuse && launch_kv_write(wp, s) != hipSuccess) return PA_ERR_LAUNCH;
     // The side streams are made on the first bf16 call of any kind: HIP deals
     // streams to the process's few hardware queues in the order they are
     // created, and side streams that share a queue with the caller's stream
@@ -327,6 +347,13 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
     }
     if (pl.prefill) e = launch_prefill(p, s);
     q1.head_first = classes == 1;            // decode tiles have the chip to themselves
+    if (fuse) {
+      q1.new_k = wp.k_new;
+      q1.new_v = wp.v_new;
+      q1.new_slots = wp.slot_mapping;
+      q1.new_stride_tok = wp.new_stride_tok;
+      q1.new_stride_head = wp.new_stride_head;
+    }
     if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
     if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
@@ -334,9 +361,13 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                         const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
-                         int64_t new_stride_head, const pa_dims* dims, pa_dtype dtype, void* stream) {
+// Checks and launch parameters of a slot-mapped write of num_tokens new rows
+// (kv_cache_write; also the new rows of paged_attention_opts).  PA_OK with
+// p.num_tokens == 0 means there is nothing to write.
+static pa_status kv_write_setup(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
+                                const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
+                                int64_t new_stride_head, const pa_dims* dims, pa_dtype dtype, KvWriteParams& p) {
+  p = KvWriteParams{};
   if (!dims) return PA_ERR_NULL;
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || new_stride_tok < 0 || new_stride_head < 0) return PA_ERR_SHAPE;
@@ -355,11 +386,10 @@ pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, voi
     return PA_ERR_SHAPE;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return PA_ERR_UNSUPPORTED;
-  KvWriteParams p{};
   p.k_new = k_new;
   p.v_new = v_new;
-  p.k_pool = k_pool;
-  p.v_pool = v_pool;
+  p.k_pool = const_cast<void*>(k_pool);
+  p.v_pool = const_cast<void*>(v_pool);
   p.slot_mapping = slot_mapping;
   p.new_stride_tok = new_stride_tok;
   p.new_stride_head = new_stride_head;
@@ -372,6 +402,16 @@ pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, voi
   p.page_size = dims->page_size;
   p.num_pages = dims->num_pages;
   p.elem_bytes = dtype == PA_BF16 ? 2 : 4;
+  return PA_OK;
+}
+
+pa_status kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                         const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
+                         int64_t new_stride_head, const pa_dims* dims, pa_dtype dtype, void* stream) {
+  KvWriteParams p;
+  const pa_status st = kv_write_setup(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, new_stride_tok,
+                                      new_stride_head, dims, dtype, p);
+  if (st != PA_OK || p.num_tokens == 0) return st;
   return launch_kv_write(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

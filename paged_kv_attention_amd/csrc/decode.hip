@@ -96,8 +96,9 @@ struct DecodeChunk {
 // WIN: the launch has a sliding window (p.window > 0); KQ: the pools' code
 // type (KvCode).  The plain instantiation carries none of their code.
 // NB: register chunks per wave, 0 for the code type's default (see the main
-// loop).
-template <int D, int NT, bool WIN, int KQ, int NB = 0>
+// loop).  FW: the launch also writes the step's new rows (bf16 pools, 16-row
+// tiles; see the main loop).
+template <int D, int NT, bool WIN, int KQ, int NB = 0, bool FW = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D, KQ>;
   constexpr bool QUANT = KQ != KV_BF16;
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int k_begin = WIN ? max(pg0 * ps, wlo & ~15) : pg0 * ps;   // 16-key tiles stay inside pages
   const int k_end = min(pg1 * ps, L);
   const int nchunks = k_end > k_begin ? (k_end - k_begin + C::KC - 1) / C::KC : 0;
+
   const int causal = p.causal;
   const int diag = L - n;                       // token t sees keys j <= diag + t
   // keys below mask_lim are visible to every row of this tile, and so are
@@ -403,6 +405,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   // heads of up to 128 dims).
   constexpr int NBUF = NB ? NB : C::NBUF;
   DecodeChunk<D, KQ> buf[NBUF];
+
+  if constexpr (FW) {
+    // The step's new rows of KV head g whose positions fall in this split's
+    // pages go to their slots before any key is read (the write of
+    // kv_cache_write, done by this launch: no other workgroup reads those
+    // positions).  Both rows are loaded before either is stored.  A
+    // workgroup barrier orders the stores before every wave's loads: only
+    // this workgroup reads the rows, so no agent-scope fence (which would
+    // write back the XCD's L2) is needed.
+    constexpr int CPR = D * 2 / 16;             // 16-byte chunks per row
+    for (int c = threadIdx.x; c < n * CPR; c += 256) {
+      const int t = c / CPR, cc = c % CPR;
+      const int lp = (L - n + t) / ps;
+      const int slot = p.new_slots[s0 + t];
+      if (L - n + t >= 0 && lp >= pg0 && lp < pg1 && slot >= 0 && slot < p.num_pages * ps) {
+        const int64_t src = (int64_t)(s0 + t) * p.new_stride_tok + (int64_t)g * p.new_stride_head + 8 * cc;
+        const int64_t dst = (int64_t)(slot / ps) * p.kv_stride_page + (int64_t)(slot % ps) * p.kv_stride_slot +
+                            (int64_t)g * p.kv_stride_head + 8 * cc;
+        const u32x4 kx = *(const u32x4*)((const __bf16*)p.new_k + src);
+        const u32x4 vx = *(const u32x4*)((const __bf16*)p.new_v + src);
+        *(u32x4*)((__bf16*)p.k_pool + dst) = kx;
+        *(u32x4*)((__bf16*)p.v_pool + dst) = vx;
+      }
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j)
     if (wave + 4 * j < nchunks) load(wave + 4 * j, buf[j]);
@@ -535,6 +563,20 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
     default:
       // two chunks per wave in flight for split launches (see the main loop);
       // 256-dim heads do not have the registers for it
+      if constexpr (NT == 1) {
+        if (p.new_k) {                           // the step's new rows written by this launch
+          if constexpr (D <= 128) {
+            if (p.num_splits > 1) {
+              if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2, true>), grid, dim3(256), 0, st, p);
+              else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 2, true>), grid, dim3(256), 0, st, p);
+              break;
+            }
+          }
+          if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 0, true>), grid, dim3(256), 0, st, p);
+          else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 0, true>), grid, dim3(256), 0, st, p);
+          break;
+        }
+      }
       if constexpr (NT == 1 && D <= 128) {
         if (p.num_splits > 1) {
           if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2>), grid, dim3(256), 0, st, p);

@@ -64,6 +64,13 @@ struct AttnParams {
                             // the output instead of writing a partial
   int32_t head_first;       // 16-row decode tiles: grid (KV head, sequence, split) instead of
                             // (split, KV head, sequence)
+  // 16-row decode tiles, bf16 pools: the step's new K/V rows, written by the
+  // workgroup whose pages hold each token's position before it attends
+  // (NULL = none); element strides of the [N, Hkv, D] rows
+  const void* new_k;
+  const void* new_v;
+  const int32_t* new_slots;
+  int64_t new_stride_tok, new_stride_head;
 };
 
 // First page of the split ranges of a sequence with context L and n step

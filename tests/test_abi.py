@@ -83,6 +83,18 @@ def test_option_errors_return_status_without_launch():
     assert call(PaAttnOpts(0, 0, 18)) == pa.PA_ERR_UNSUPPORTED              # sinks not 4-byte aligned
     assert call(PaAttnOpts(0, 0, None), _dims(head_dim=96)) == pa.PA_ERR_UNSUPPORTED
     assert call(PaAttnOpts(16, 0, None), _dims(num_seqs=0, num_tokens=0)) == pa.PA_OK
+    # the step's new rows: all three pointers, 16-byte alignment, whole-vector strides
+    o = PaAttnOpts(0, 0, None)
+    o.k_new, o.v_new, o.slot_mapping, o.new_stride_tok, o.new_stride_head = 16, None, 16, 8 * 128, 128
+    assert call(o) == pa.PA_ERR_NULL                                        # v_new missing
+    o.v_new, o.slot_mapping = 16, None
+    assert call(o) == pa.PA_ERR_NULL                                        # slot_mapping missing
+    o.slot_mapping, o.k_new = 16, 24
+    assert call(o) == pa.PA_ERR_UNSUPPORTED                                 # k_new not 16-byte aligned
+    o.k_new, o.new_stride_head = 16, 100
+    assert call(o) == pa.PA_ERR_UNSUPPORTED                                 # stride not whole 16-byte chunks
+    o.new_stride_head = 64
+    assert call(o) == pa.PA_ERR_SHAPE                                       # head rows overlap (stride < D)
 
 
 def test_workspace_and_split_rules():
