@@ -164,20 +164,40 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnParams p) {
   // workspace rows per split: (sequence, step token) slots, or flat tokens
   const int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
   const int64_t row = p.ws_flat ? (int64_t)tok * p.num_q_heads + h : ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
+  // Splits are read in groups of 8 whose loads are all issued before any is
+  // used (one memory latency per group and pass rather than one per split);
+  // padding entries (-inf, 0) leave the sums bit for bit unchanged.
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(s * NH + row) * 2]);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = s0 + j < S ? p.ws_ml[((s0 + j) * NH + row) * 2] : kNegInf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, m[j]);
+  }
   const float Ms = M == kNegInf ? 0.f : M;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   float l = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const int64_t ri = s * NH + row;
-    const float w = fast_exp2(p.ws_ml[ri * 2] - Ms);
-    l = fmaf(w, p.ws_ml[ri * 2 + 1], l);
-    const float* a = p.ws_acc + ri * D;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float mv[8], lv[8], av[8][DPL];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, a[lane * DPL + i], acc[i]);
+    for (int j = 0; j < 8; ++j) {
+      const int64_t ri = (s0 + j) * NH + row;
+      const bool in = s0 + j < S;
+      mv[j] = in ? p.ws_ml[ri * 2] : kNegInf;
+      lv[j] = in ? p.ws_ml[ri * 2 + 1] : 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) av[j][i] = in ? p.ws_acc[ri * D + lane * DPL + i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = fast_exp2(mv[j] - Ms);
+      l = fmaf(w, lv[j], l);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, av[j][i], acc[i]);
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (BF16) {

@@ -516,18 +516,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       // this row (flat workspace rows) with the suffix state and normalise
       const int64_t NHf = (int64_t)p.num_tokens * p.num_q_heads;
       const int64_t rrow = (int64_t)tok * p.num_q_heads + head;
+      // Partials are read in groups of 8 whose loads are all issued before
+      // any is used: one memory latency per group and pass, not one per
+      // split.  Padding entries (-inf, 0) leave every sum unchanged.
+      const int np = p.merge_prefix;
       float Mx = M;
-      for (int s2 = 0; s2 < p.merge_prefix; ++s2) Mx = fmaxf(Mx, p.ws_ml[(s2 * NHf + rrow) * 2]);
+      for (int g0 = 0; g0 < np; g0 += 8) {
+        float m[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m[j] = g0 + j < np ? p.ws_ml[((g0 + j) * NHf + rrow) * 2] : kNegInf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, m[j]);
+      }
       const float Ms = Mx == kNegInf ? 0.f : Mx;
       const float e0 = fast_exp2(M - Ms);
       float Ltot = Lt * e0;
       f32x4 ot = o * e0;
-      for (int s2 = 0; s2 < p.merge_prefix; ++s2) {
-        const int64_t ri = s2 * NHf + rrow;
-        const f32x2 ml = *(const f32x2*)(p.ws_ml + ri * 2);
-        const float w = fast_exp2(ml[0] - Ms);
-        Ltot = fmaf(w, ml[1], Ltot);
-        ot += w * *(const f32x4*)(p.ws_acc + ri * D + 4 * c4);
+      for (int g0 = 0; g0 < np; g0 += 8) {
+        f32x2 ml[8];
+        f32x4 pa[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (g0 + j < np) {
+            const int64_t ri = (g0 + j) * NHf + rrow;
+            ml[j] = *(const f32x2*)(p.ws_ml + ri * 2);
+            pa[j] = *(const f32x4*)(p.ws_acc + ri * D + 4 * c4);
+          } else {
+            ml[j] = f32x2{kNegInf, 0.f};
+            pa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float w = fast_exp2(ml[j][0] - Ms);
+          Ltot = fmaf(w, ml[j][1], Ltot);
+          ot += w * pa[j];
+        }
       }
       const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
