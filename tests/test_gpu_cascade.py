@@ -60,16 +60,19 @@ def test_cascade_verify_blocks(D, ps, qlens):
     _check(w, got, label=f"cascade D {D} ps {ps}")
 
 
+# a 1,344-position prefix is cut into 11 key ranges (21 blocks of 64, two per
+# range), so the fold and the combine also meet a partial group of 8 partials
+@pytest.mark.parametrize("prefix", [1024, 1344])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_cascade_with_sinks_and_forced_suffix_splits(splits):
-    w = make_shared_prefix(seed=710, prefix_len=1024, suffix_lens=[300, 1, 700, 64, 5], query_lens=[1, 1, 5, 2, 1],
+def test_cascade_with_sinks_and_forced_suffix_splits(splits, prefix):
+    w = make_shared_prefix(seed=710, prefix_len=prefix, suffix_lens=[300, 1, 700, 64, 5], query_lens=[1, 1, 5, 2, 1],
                            num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64)
     q, k, v, bt, cl, qsl = _dev(w)
     sk = torch.randn(32, generator=torch.Generator().manual_seed(3)) * 2
     got = pa.paged_attention(q, k, v, bt, cl, qsl, w.scale, True, max_query_len=5, num_splits=splits,
-                             sinks=sk.to(DEV), shared_prefix_len=1024)
+                             sinks=sk.to(DEV), shared_prefix_len=prefix)
     torch.cuda.synchronize()
-    _check(w, got, label=f"cascade sinks splits {splits}", sinks=sk.double())
+    _check(w, got, label=f"cascade sinks splits {splits} prefix {prefix}", sinks=sk.double())
 
 
 def test_cascade_over_int8_cache():

@@ -56,7 +56,9 @@ def test_fp32_mha_and_group3_not_causal():
 
 
 # ---------------------------------------------------------------- bf16 decode / verify
-@pytest.mark.parametrize("splits", [0, 1, 3, 8])
+# 11 and 19 splits: the merge reads splits in groups of 8, so these cover
+# whole groups followed by a partial one
+@pytest.mark.parametrize("splits", [0, 1, 3, 8, 11, 19])
 def test_bf16_decode_ragged(splits):
     lens = [1, 2, 63, 64, 65, 700, 2048, 4096, 33, 129]
     w = poison_unused(_custom(40, lens, [1] * len(lens)))
