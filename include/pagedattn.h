@@ -13,7 +13,10 @@
  * - All buffers are device memory owned by the caller.  The library
  *   allocates no memory, keeps no per-call state and never reads device
  *   memory back in paged_attention / kv_cache_write, so both can be captured
- *   in a hipGraph.  Cached per device: the CU count, and two side streams
+ *   in a hipGraph.  Its one device buffer of its own is the static scratch
+ *   array of paged_attention_noalloc (PA_STATIC_SCRATCH_BYTES per device,
+ *   loaded with the library's code).  Cached per device: the CU count, the
+ *   address of that array, and two side streams
  *   with three events (default priority), created by the first bf16
  *   paged_attention call made outside graph capture and kept until the
  *   process ends.  They serve calls that launch more than one tile class
@@ -54,7 +57,9 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 3,   /* dtype, head_dim or page_size not built            */
   PA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required       */
   PA_ERR_LAUNCH = 5,        /* the HIP runtime refused a launch                  */
-  PA_ERR_INVALID_DATA = 6   /* pa_validate only: device metadata out of range   */
+  PA_ERR_INVALID_DATA = 6,  /* pa_validate only: device metadata out of range   */
+  PA_ERR_SCRATCH_LIMIT = 7  /* paged_attention_noalloc: the call's split partials
+                               need more than PA_STATIC_SCRATCH_BYTES             */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -120,6 +125,34 @@ pa_status paged_attention(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* query_start_loc, float scale, int causal,
                           void* out, void* workspace, size_t workspace_bytes,
                           const pa_dims* dims, pa_dtype dtype, void* stream);
+
+/*
+ * paged_attention_noalloc -- paged_attention for callers that cannot allocate
+ * device memory (code under hipGraph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation, arguments, layouts, kernels
+ * and results as paged_attention with the same dims, but no workspace
+ * argument.  The split partials go to the library's own static device buffer
+ * of PA_STATIC_SCRATCH_BYTES per device (a file-scope array loaded with the
+ * library, held until the process ends); its device address is looked up
+ * once per device, on the first call made on that device.  The call
+ * allocates nothing: no hipMalloc / hipFree, no stream or event creation (all
+ * launches go to `stream`, one after another, even for mixed batches).
+ *
+ * Limit: a call whose split partials need more than PA_STATIC_SCRATCH_BYTES
+ * (pa_workspace_size(dims, dtype) > PA_STATIC_SCRATCH_BYTES) returns
+ * PA_ERR_SCRATCH_LIMIT with nothing launched.
+ * Sharing: every call on one device uses the same buffer and it keeps the
+ * last call's contents.  Calls that overlap in time on one device (on
+ * different streams without ordering between them, or from several threads)
+ * race on it and their results are undefined; calls ordered on one stream
+ * are safe.  Nothing in the buffer needs to start at zero: every partial a
+ * call reads was written earlier in the same call.
+ */
+#define PA_STATIC_SCRATCH_BYTES (32u << 20)
+pa_status paged_attention_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start_loc, float scale, int causal, void* out,
+                                  const pa_dims* dims, pa_dtype dtype, void* stream);
 
 /*
  * Quantized KV cache (page "32. Production attention kernels", Quantized KV

@@ -17,10 +17,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
-PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_INVALID_DATA = range(7)
+(PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_INVALID_DATA,
+ PA_ERR_SCRATCH_LIMIT) = range(8)
+# bytes of the library's static device buffer used by paged_attention_noalloc
+STATIC_SCRATCH_BYTES = 32 << 20
 PA_F32, PA_BF16 = 0, 1
 
-EXPORTED = ("paged_attention", "paged_attention_opts", "kv_cache_write", "kv_cache_write_quant", "pa_workspace_size",
+EXPORTED = ("paged_attention", "paged_attention_opts", "paged_attention_noalloc", "kv_cache_write", "kv_cache_write_quant", "pa_workspace_size",
             "pa_workspace_size_opts", "pa_choose_splits", "pa_validate", "pa_validate_opts", "pa_status_string",
             "pa_device_cu_count", "pa_read_probe")
 
@@ -128,6 +131,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_opts.argtypes = [vp, vp, vp, i32p, i32p, i32p, ctypes.c_float, ctypes.c_int, vp, vp,
                                          ctypes.c_size_t, ctypes.POINTER(PaDims), ctypes.c_int,
                                          ctypes.POINTER(PaAttnOpts), vp]
+    lib.paged_attention_noalloc.restype = ctypes.c_int
+    lib.paged_attention_noalloc.argtypes = [vp, vp, vp, i32p, i32p, i32p, ctypes.c_float, ctypes.c_int, vp,
+                                            ctypes.POINTER(PaDims), ctypes.c_int, vp]
     lib.kv_cache_write_quant.restype = ctypes.c_int
     lib.kv_cache_write_quant.argtypes = [vp, vp, vp, vp, i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.POINTER(PaDims), ctypes.c_int, ctypes.POINTER(PaKvQuant), vp]
@@ -323,6 +329,33 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                  ctypes.byref(dims), code, _stream_ptr(stream))
     if st != PA_OK:
         raise PagedAttnError(st, "paged_attention")
+    return out
+
+
+def paged_attention_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                            scale: Optional[float] = None, causal: bool = True, *, out: torch.Tensor,
+                            max_query_len: Optional[int] = None, num_splits: int = 0, stream=None) -> torch.Tensor:
+    """``paged_attention`` without a workspace: the split partials go to the
+    library's static device buffer (``STATIC_SCRATCH_BYTES`` per device), so
+    the call allocates nothing.  ``out`` must be given.  Calls that overlap in
+    time on one device race on that buffer."""
+    lib = load_library()
+    if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
+    if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype or out.dtype != q.dtype:
+        raise TypeError("q, out and the pools must share one dtype")
+    dims = make_dims(q, k_pool, block_tables, out=out, max_query_len=max_query_len, num_splits=num_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    st = lib.paged_attention_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                     _i32(block_tables, "block_tables").data_ptr(),
+                                     _i32(context_lens, "context_lens").data_ptr(),
+                                     _i32(query_start_loc, "query_start_loc").data_ptr(), float(scale),
+                                     1 if causal else 0, out.data_ptr(), ctypes.byref(dims), _dtype_code(q.dtype),
+                                     _stream_ptr(stream))
+    if st != PA_OK:
+        raise PagedAttnError(st, "paged_attention_noalloc")
     return out
 
 

@@ -97,11 +97,42 @@ static SideStreams* lock_side_streams(hipStream_t caller) {
   return &ss;
 }
 
+// Device memory of paged_attention_noalloc: the split partials of a call go
+// here instead of a caller's workspace.  One copy per device, at its own
+// address, loaded with the library's code and held until the process ends.
+// Host code never uses the name itself for device memory (on the host it is
+// only a stand-in): the device address comes from hipGetSymbolAddress, once
+// per device, and is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device, or nullptr.
+static void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace pa
 
 using namespace pa;
 
 extern "C" {
+static pa_status attention_impl(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
+                                void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims,
+                                pa_dtype dtype, const pa_attn_opts* opts, hipStream_t stream, bool side_ok);
 static pa_status kv_write_setup(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
                                 const int32_t* slot_mapping, int32_t num_tokens, int64_t new_stride_tok,
                                 int64_t new_stride_head, const pa_dims* dims, pa_dtype dtype, KvWriteParams& p);
@@ -116,6 +147,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_INVALID_DATA: return "device metadata out of range";
+    case PA_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -155,6 +187,32 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
                                const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
                                void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims,
                                pa_dtype dtype, const pa_attn_opts* opts, void* stream) {
+  return attention_impl(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale, causal, out, workspace,
+                        workspace_bytes, dims, dtype, opts, (hipStream_t)stream, true);
+}
+
+pa_status paged_attention_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start_loc, float scale, int causal, void* out,
+                                  const pa_dims* dims, pa_dtype dtype, void* stream) {
+  pa_status st = check_dims(dims, dtype);
+  if (st != PA_OK) return st;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  // the split partials this call needs must fit the static buffer
+  const size_t need = make_plan(dims, dtype, cu_count()).workspace_bytes;
+  if (need > (size_t)PA_STATIC_SCRATCH_BYTES) return PA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_address())) return PA_ERR_LAUNCH;
+  return attention_impl(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale, causal, out, ws,
+                        ws ? (size_t)PA_STATIC_SCRATCH_BYTES : 0, dims, dtype, nullptr, (hipStream_t)stream, false);
+}
+
+// The body of paged_attention_opts.  side_ok = false keeps every launch on
+// `stream`: the side streams are neither created nor used.
+static pa_status attention_impl(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start_loc, float scale, int causal,
+                                void* out, void* workspace, size_t workspace_bytes, const pa_dims* dims,
+                                pa_dtype dtype, const pa_attn_opts* opts, hipStream_t stream, bool side_ok) {
   pa_status st = check_dims(dims, dtype);
   if (st != PA_OK) return st;
   if (!isfinite(scale)) return PA_ERR_SHAPE;
@@ -244,7 +302,7 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
     p.k_smooth = kq->k_smooth;
   }
 
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   hipError_t e = hipSuccess;
   if (prefix_len > 0) {
     // cascade: prefix pass over all query tokens (split slots 0..Sp-1), the
@@ -314,7 +372,7 @@ pa_status paged_attention_opts(const void* q, const void* k_pool, const void* v_
     // created, and side streams that share a queue with the caller's stream
     // run their launches one after the other (the mixed batch measured 270
     // instead of 171 us with side streams made after two other streams).
-    SideStreams* ss = lock_side_streams(s);
+    SideStreams* ss = side_ok ? lock_side_streams(s) : nullptr;
     if (ss && classes < 2) {
       ss->mu.unlock();
       ss = nullptr;

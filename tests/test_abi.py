@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert pa.status_string(pa.PA_OK) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
     assert pa.status_string(99) == "unknown status"
 
