@@ -56,7 +56,7 @@ from typing import Iterable, List, Optional, Sequence
 import numpy as np
 import torch
 
-__all__ = ["attention_f64", "brute_force", "split_combine_f64", "kv_write_ref", "visible_keys"]
+__all__ = ["attention_f64", "brute_force", "split_combine_f64", "kv_write_ref"]
 
 
 def _seq_meta(block_tables, context_lens, query_start_loc, page_size):
@@ -68,14 +68,6 @@ def _seq_meta(block_tables, context_lens, query_start_loc, page_size):
         L = max(0, min(lens[b], W * page_size))
         out.append((qsl[b], qsl[b + 1] - qsl[b], L))
     return out
-
-
-def visible_keys(L: int, n: int, t: int, causal: bool, window: int = 0) -> int:
-    """Number of visible keys of token t of an n-token step over context L."""
-    pos = L - n + t
-    hi = L if not causal else max(0, min(L, pos + 1))
-    lo = max(0, pos - window + 1) if window > 0 else 0
-    return max(0, hi - lo)
 
 
 def _gather(pool: torch.Tensor, table_row: torch.Tensor, L: int) -> torch.Tensor:
@@ -122,6 +114,7 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
         # GQA: query head h uses KV head h // G (repeat_interleave over the group)
         Kh = Kb.repeat_interleave(G, dim=1).permute(1, 0, 2)   # [Hq, L, D]
         Vh = Vb.repeat_interleave(G, dim=1).permute(1, 0, 2)
+        KhT = Kh.transpose(1, 2).contiguous()                  # [Hq, D, L]: a copy, so the products run fast
         for c0 in range(0, len(ts), chunk):
             tc = torch.tensor(ts[c0:c0 + chunk], dtype=torch.int64)
             pos = L - n + tc                                   # [T]
@@ -129,7 +122,7 @@ def attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
             if hi <= 0:
                 continue
             Q = q[s0 + tc].to(torch.float64).permute(1, 0, 2)  # [Hq, T, D]
-            x = sc * torch.matmul(Q, Kh[:, :hi].transpose(1, 2))   # [Hq, T, hi]
+            x = sc * torch.matmul(Q, KhT[:, :, :hi])           # [Hq, T, hi]
             j = torch.arange(hi)
             vis = j[None, :] < L
             if causal:

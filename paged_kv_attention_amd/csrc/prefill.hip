@@ -7,9 +7,10 @@
 // questions: GQA packing in the prefill kernel; page "32. Production attention
 // kernels", One kernel for the whole batch).  Each wave owns 32 rows.
 //
-// The tile walks the sequence's pages in 64-key blocks and stops at the key
-// its last token can see (page "32. Production attention kernels": the key
-// loop stops at the tile's last query).  With bf16 pools and 128-dim heads
+// The tile walks the sequence's pages in 64-key blocks and ends with the
+// block holding the newest key that its last token may attend to, since no
+// row of the tile sees anything later (page "32. Production attention
+// kernels", One kernel for the whole batch: the causal bound of a query tile).  With bf16 pools and 128-dim heads
 // the blocks go from global memory straight into LDS (global_load_lds, no
 // register staging, no LDS stores) through a four-stage ring, three blocks
 // ahead of the one being computed; rows are 256 bytes with their 16-byte

@@ -2,6 +2,9 @@
 compare with the float64 oracle."""
 from __future__ import annotations
 
+import ctypes
+import dataclasses
+import json
 import sys
 from typing import Iterable, Optional
 
@@ -12,6 +15,17 @@ from oracle import attention_f64
 from workloads import Workload
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+
+# The float64 oracle allocates large temporaries per query chunk.  Keeping
+# freed host memory in the process heap (instead of returning it to the
+# kernel) spares a fresh page fault per byte on every chunk; on the full-size
+# prefill checks this takes a sequence from ~23 s to ~9 s of host time.
+try:
+    _libc = ctypes.CDLL("libc.so.6")
+    _libc.mallopt(-3, 1 << 30)       # M_MMAP_THRESHOLD: blocks up to 1 GiB come from the heap
+    _libc.mallopt(-1, 2 ** 31 - 1)   # M_TRIM_THRESHOLD: never hand the heap's top back
+except OSError:
+    pass
 
 
 def to_dev(w: Workload, layout: str = "head_major"):
@@ -57,7 +71,60 @@ def check(w: Workload, got: torch.Tensor, tokens: Optional[Iterable[int]] = None
     r = ref.index_select(0, idx)
     assert not torch.isnan(g).any(), f"{label}: NaN in output"
     assert not torch.isinf(g).any(), f"{label}: Inf in output"
-    err = torch.max(torch.abs(g - r)).item() if g.numel() else 0.0
-    print(f"[parity] {label or w.name}: max abs err {err:.3e} (tol {tol:g})", file=sys.stderr, flush=True)
+    err = log_worst_row(w, g, r, toks, label or w.name, tol)
     assert err <= tol, f"{label}: max abs err {err} > {tol}"
     return err
+
+
+def log_worst_row(w: Workload, g: torch.Tensor, r: torch.Tensor, toks, label: str, tol: float) -> float:
+    """Print one JSON line with the case's max abs error and its worst row:
+    flat token, query head, the sequence's context length L, the largest
+    |o| of the oracle's row, and the row's error.  Returns the max error."""
+    if not g.numel():
+        return 0.0
+    row_err = torch.abs(g - r).amax(-1)                        # [tokens, Hq]
+    flat = int(torch.argmax(row_err))
+    ti, h = divmod(flat, row_err.shape[1])
+    tok = int(toks[ti])
+    qsl = w.query_start_loc.tolist()
+    b = max(i for i in range(len(qsl) - 1) if qsl[i] <= tok)
+    err = float(row_err.view(-1)[flat])
+    rec = {"case": label, "max_abs_err": err, "tol": tol, "rows": int(row_err.numel()),
+           "worst": {"token": tok, "head": h, "L": int(w.context_lens[b]), "pos": int(w.context_lens[b]) - (qsl[b + 1] - qsl[b]) + tok - qsl[b],
+                     "ref_abs_max": float(r[ti, h].abs().max()), "err": err}}
+    print("[parity] " + json.dumps(rec), file=sys.stderr, flush=True)
+    return err
+
+
+def seq_slice(w: Workload, b: int) -> Workload:
+    """Sequence b of a workload alone (same pools), as a one-sequence batch."""
+    qsl = w.query_start_loc.tolist()
+    s0, s1 = qsl[b], qsl[b + 1]
+    return dataclasses.replace(w, q=w.q[s0:s1], block_tables=w.block_tables[b:b + 1],
+                               context_lens=w.context_lens[b:b + 1],
+                               query_start_loc=torch.tensor([0, s1 - s0], dtype=torch.int32))
+
+
+def check_every_row(w: Workload, got: torch.Tensor, label: str, tol: Optional[float] = None, window: int = 0,
+                    sinks: Optional[torch.Tensor] = None, chunk: int = 128) -> float:
+    """Compare every written row of `got` with the oracle, one sequence at a
+    time (progress printed per sequence), after checking that no row of the
+    whole output holds NaN or Inf: run with an output pre-filled with NaN, a
+    row no tile wrote fails here."""
+    tol = TOL[w.dtype] if tol is None else tol
+    assert not torch.isnan(got).any(), f"{label}: NaN in output (a row was not written)"
+    assert not torch.isinf(got).any(), f"{label}: Inf in output"
+    qsl = w.query_start_loc.tolist()
+    worst = 0.0
+    for b in range(w.num_seqs):
+        if qsl[b + 1] == qsl[b]:
+            continue
+        ws = seq_slice(w, b)
+        ref = attention_f64(ws.q, ws.k_pool, ws.v_pool, ws.block_tables, ws.context_lens, ws.query_start_loc,
+                            ws.scale, causal=ws.causal, chunk=chunk, window=window,
+                            sinks=None if sinks is None else sinks.to(torch.float32).double())
+        g = got[qsl[b]:qsl[b + 1]].double()
+        err = log_worst_row(w, g, ref, list(range(qsl[b], qsl[b + 1])), f"{label} seq {b}", tol)
+        worst = max(worst, err)
+        assert err <= tol, f"{label} seq {b}: max abs err {err} > {tol}"
+    return worst

@@ -13,7 +13,7 @@ import torch
 
 import paged_kv_attention_amd as pa
 from gpu_util import TOL
-from oracle import attention_f64, quantize_kv, dequantize
+from oracle import attention_f64, quantize_head_vectors, dequantize
 from workloads import make_shared_prefix, make_cascade_decode
 
 pytestmark = pytest.mark.gpu
@@ -79,8 +79,8 @@ def test_cascade_over_int8_cache():
     w = make_shared_prefix(seed=720, prefix_len=2048, suffix_lens=[100, 33, 257], query_lens=[1, 4, 1],
                            num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64)
     P, ps, Hkv, D = w.k_pool.shape
-    kc, ks = quantize_kv(w.k_pool.reshape(P * ps, Hkv, D), "int8")
-    vc, vs = quantize_kv(w.v_pool.reshape(P * ps, Hkv, D), "int8")
+    kc, ks = quantize_head_vectors(w.k_pool.reshape(P * ps, Hkv, D), "int8")
+    vc, vs = quantize_head_vectors(w.v_pool.reshape(P * ps, Hkv, D), "int8")
     kc, vc, ks, vs = kc.reshape(P, ps, Hkv, D), vc.reshape(P, ps, Hkv, D), ks.reshape(P, ps, Hkv), vs.reshape(P, ps, Hkv)
     kd = pa.empty_code_pool(P, ps, Hkv, D, "int8", DEV)
     vd = pa.empty_code_pool(P, ps, Hkv, D, "int8", DEV)

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import paged_kv_attention_amd as pa
-from gpu_util import TOL
-from oracle import attention_f64, quantize_kv, kv_write_quant_ref, dequantize
+from gpu_util import TOL, check_every_row
+from oracle import attention_f64, quantize_head_vectors, kv_write_quant_ref, dequantize
 from workloads import make_custom, make
 
 pytestmark = pytest.mark.gpu
@@ -32,8 +32,8 @@ def _smooth(Hkv, D, seed=4):
 def _quantized_cache(w, kind, smooth=None):
     """Oracle codes and scales of a workload's pools: [P, ps, Hkv, D], [P, ps, Hkv]."""
     P, ps, Hkv, D = w.k_pool.shape
-    kc, ks = quantize_kv(w.k_pool.reshape(P * ps, Hkv, D), kind, smooth)
-    vc, vs = quantize_kv(w.v_pool.reshape(P * ps, Hkv, D), kind)
+    kc, ks = quantize_head_vectors(w.k_pool.reshape(P * ps, Hkv, D), kind, smooth)
+    vc, vs = quantize_head_vectors(w.v_pool.reshape(P * ps, Hkv, D), kind)
     return (kc.reshape(P, ps, Hkv, D), vc.reshape(P, ps, Hkv, D), ks.reshape(P, ps, Hkv), vs.reshape(P, ps, Hkv))
 
 
@@ -200,11 +200,17 @@ def test_mixed_batch_quantized_window_sinks(kind):
     _check(got, _ref(w, kc, vc, ks, vs, sm, window=300, sinks=sk.double()), label=f"{kind} mixed window sinks")
 
 
-def test_prefill_4x8192_int8_sampled():
-    """The 4 x 8192 causal prefill over an int8 cache, sampled rows."""
+def test_prefill_4x8192_int8_every_row():
+    """The 4 x 8192 causal prefill over an int8 cache, as the bench times it:
+    every row against the oracle over the dequantized cache, the output
+    pre-filled with NaN so a row no tile writes fails."""
     w = make(5)
     kc, vc, ks, vs = _quantized_cache(w, "int8")
     kd, vd, kq = _to_dev_cache(kc, vc, ks, vs, "int8")
-    got = _run(w, kd, vd, kq)
-    toks = [b * 8192 + t for b in range(4) for t in (0, 1, 255, 256, 4095, 8191)]
-    _check(got, _ref(w, kc, vc, ks, vs, tokens=toks), tokens=toks, label="4x8192 int8 prefill (sampled)")
+    q = w.q.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    pa.paged_attention(q, kd, vd, w.block_tables.to(DEV), w.context_lens.to(DEV), w.query_start_loc.to(DEV),
+                       w.scale, w.causal, out=out, max_query_len=w.max_query_len, kv_quant=kq)
+    torch.cuda.synchronize()
+    wd = dataclasses.replace(w, k_pool=dequantize(kc, ks), v_pool=dequantize(vc, vs))
+    check_every_row(wd, out.cpu(), tol=TOL[torch.bfloat16], label="4x8192 int8 prefill every row")

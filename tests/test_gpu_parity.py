@@ -17,7 +17,7 @@ import torch
 import paged_kv_attention_amd as pa
 from oracle import kv_write_ref
 from workloads import make, make_custom, poison_unused
-from tests.gpu_util import run_lib, check, to_dev
+from tests.gpu_util import run_lib, check, check_every_row, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -288,21 +288,11 @@ def test_config4_full_and_shuffled():
     check(w2, run_lib(w2), label="C4 shuffled")
 
 
-def _prefill_sample_tokens(w, per_seq=12):
-    qsl = w.query_start_loc.tolist()
-    g = torch.Generator().manual_seed(77)
-    toks = []
-    for b in range(w.num_seqs):
-        n = qsl[b + 1] - qsl[b]
-        fixed = [0, 1, 31, 32, 127, 128, n // 2, n - 129, n - 2, n - 1]
-        rnd = torch.randint(0, n, (per_seq,), generator=g).tolist()
-        toks += [qsl[b] + t for t in fixed + rnd if 0 <= t < n]
-    return toks
-
-
 @pytest.mark.parametrize("config", [5, 6])
-def test_config5_prefill_sampled(config):
+def test_config5_prefill_every_row(config):
+    """The 4 x 8192 causal prefills (D 128 and the D 256 variant) in the launch
+    configuration the bench times: every row against the oracle, the output
+    pre-filled with NaN so a row no tile writes fails."""
     w = make(config)
-    got = run_lib(w)
-    assert not torch.isnan(got).any()
-    check(w, got, tokens=_prefill_sample_tokens(w), label=f"C{config} sampled")
+    got = run_lib(w, out_fill=float("nan"))
+    check_every_row(w, got, label=f"C{config} every row")

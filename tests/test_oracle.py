@@ -113,6 +113,12 @@ def test_closed_form_two_keys():
     out3 = attention_f64(q, k, v, bt, lens, qsl, 0.5, causal=False)
     w1 = math.exp(3.5) / (1.0 + math.exp(3.5))
     assert abs(out3[0, 0, 1].item() - 8.0 * w1) <= 1e-13
+    # the scalar-loop oracle meets the same closed forms
+    bf = brute_force(q, k, v, bt, lens, qsl, 0.5)
+    assert bf[0][0] == [4.0, 0.0]
+    assert abs(bf[1][0][0] - 4.0 / (1.0 + e)) <= 1e-15 and abs(bf[1][0][1] - 8.0 * e / (1.0 + e)) <= 1e-14
+    assert abs(brute_force(q2, k, v, bt, lens, qsl, 0.5)[1][0][0] - 4.0 * e / (1.0 + e)) <= 1e-14
+    assert abs(brute_force(q, k, v, bt, lens, qsl, 0.5, causal=False)[0][0][1] - 8.0 * w1) <= 1e-13
 
 
 def test_single_key_returns_its_value_row():

@@ -25,7 +25,7 @@ import os
 import pytest
 import torch
 
-from oracle import quantize_kv, kv_write_quant_ref, dequantize, attention_f64, KV_QMAX
+from oracle import quantize_head_vectors, kv_write_quant_ref, dequantize, attention_f64, KV_QMAX
 from workloads import make_custom
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
@@ -41,7 +41,7 @@ def _x(seed, T=37, Hkv=3, D=64, spread=3.0):
 
 def test_int8_reconstruction_bound_and_edge():
     x = _x(1)
-    codes, scale = quantize_kv(x, "int8")
+    codes, scale = quantize_head_vectors(x, "int8")
     assert codes.dtype == torch.int8 and scale.dtype == torch.float32
     rec = codes.double() * scale.double().unsqueeze(-1)
     err = (rec - x.double()).abs()
@@ -56,7 +56,7 @@ def test_int8_reconstruction_bound_and_edge():
 
 def test_fp8_reconstruction_bound_and_edge():
     x = _x(2)
-    codes, scale = quantize_kv(x, "fp8")
+    codes, scale = quantize_head_vectors(x, "fp8")
     assert codes.dtype == torch.float8_e4m3fn
     s = scale.double().unsqueeze(-1)
     vals = codes.double()                                   # in code units
@@ -85,7 +85,7 @@ def test_smoothing_leaves_scores_unchanged():
     smooth = torch.rand(Hkv, D, generator=g) * 3 + 0.25
     P, ps = w.k_pool.shape[:2]
     flat = w.k_pool.reshape(P * ps, Hkv, D)
-    c_s, s_s = quantize_kv(flat, "int8", smooth)
+    c_s, s_s = quantize_head_vectors(flat, "int8", smooth)
     k_smoothed = dequantize(c_s.reshape(P, ps, Hkv, D), s_s.reshape(P, ps, Hkv), smooth)
     # the smoothed cache stands for keys close to the originals ...
     step = (s_s.double().reshape(P, ps, Hkv, 1) * smooth.double().reshape(1, 1, Hkv, D)) * 0.5
@@ -118,7 +118,7 @@ def test_write_map(kind):
     vn = torch.randn(4, Hkv, D, generator=g)
     slots = torch.tensor([7, -1, 0, 19], dtype=torch.int32)
     kc2, vc2, ks2, vs2 = kv_write_quant_ref(kn, vn, kc, vc, ks, vs, slots, kind)
-    c, s = quantize_kv(kn, kind)
+    c, s = quantize_head_vectors(kn, kind)
     for i, sl in enumerate(slots.tolist()):
         if sl < 0:
             continue
