@@ -13,7 +13,7 @@ namespace pa {
 hipError_t launch_decode(const AttnParams& p, int nt, hipStream_t st);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t st);
 hipError_t launch_prefix(const AttnParams& p, hipStream_t st);
-hipError_t launch_f32(const AttnParams& p, int max_q, hipStream_t st);
+hipError_t launch_f32(const AttnParams& p, hipStream_t st);
 hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
 hipError_t launch_kv_write_quant(const KvWriteParams& p, hipStream_t st);
@@ -350,7 +350,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
   }
   if (dtype == PA_F32) {
     if (wp.num_tokens > 0) e = launch_kv_write(wp, s);
-    if (e == hipSuccess) e = launch_f32(p, pl.mql, s);
+    if (e == hipSuccess) e = launch_f32(p, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, false, s);
   } else {
     AttnParams q1 = p;                       // 16-row decode tiles

@@ -1,140 +1,271 @@
-// Float32 paged attention on the vector ALUs (gfx950).
+// Float32 paged attention, GQA-packed, on the fp32 matrix cores (gfx950).
 //
-// Float32 has no MFMA path worth its precision cost here, so each query row
-// (token, query head, split) is one wave.  The wave walks its split's keys in
-// chunks of 64: lane j scores key j of the chunk against the row's query
-// (held in LDS, read as a broadcast), the chunk's maximum and the softmax
-// state are wave reductions, and lane d accumulates output dims d, d+64, ...
-// with the chunk's probabilities read lane by lane.  Everything stays float32
-// (page "paged-attn-xpu", Requirements and limits: scores and softmax state
-// float32, split partials float32) and only keys below the row's visible end
-// are ever read, so slots past the context are never touched.  With a
-// sliding window a row also starts at its own window start; split 0 folds an
-// attention sink into its state as one more score with no value row (page
-// "32. Production attention kernels", window mask and Stretch exercises).
+// One workgroup per (split x 16-row tile, KV head g, sequence b).  The rows of
+// a tile are the sequence's step tokens times the G query heads that share KV
+// head g, row r = token (r / G), head g*G + r % G; a sequence with more than
+// 16 such rows takes several tiles.  Every K/V row of the split is read once
+// for all rows of the tile (page "Attention kernels", Decode: GQA packing and
+// split-KV; page "Attention and KV Cache", Multi-head, GQA, and MQA: the
+// heads of a group read the same K/V).
+//
+// The tile's keys are cut into 16-key chunks; wave w of NW takes chunks w,
+// w + NW, ... with its own online-softmax state, two chunks in registers at
+// a time (the next one is loaded while this one is computed).  Per chunk:
+//   S^T[16 keys x 16 rows] = K . Q^T    v_mfma_f32_16x16x4_f32, K loaded from
+//                                       the page in 16-byte pieces straight
+//                                       into the A operand, Q^T held in the B
+//                                       operand (4 dims per k-step);
+//   mask (only chunks that reach the causal diagonal, the range end or a
+//   window edge); m' = max(m, rowmax), alpha = exp2(m - m'),
+//   p = exp2(s - m') with the -inf guard;
+//   O^T[D x 16 rows] += V^T . P^T       the same MFMA; P^T is already in the
+//                                       B-operand layout of S^T's accumulator
+//                                       registers, and lane (i, k) reads the
+//                                       value V[key 4k + r][dim 16 t + i];
+// V rows outside the tile's key range are selected to zero first, so a NaN
+// in an unused slot never reaches an output.  Everything stays float32 (page
+// "paged-attn-xpu", Requirements and limits: scores, softmax state and split
+// partials in float32).  The waves merge their states in LDS in a fixed
+// order.  With one split the normalised rows are written directly (one
+// launch, no combine); otherwise the unnormalised partial (acc, m, l) goes to
+// the workspace, and a split without keys writes the neutral (0, -inf, 0).
+// A sliding window starts the key range at the tile's first window start and
+// masks per row; split 0 folds an attention sink into its state as one more
+// score with no value row (page "32. Production attention kernels", window
+// mask and Stretch exercises).
+#include <limits.h>
+
 #include "pa_device.h"
 
 namespace pa {
 
+// Waves per workgroup: enough to spread a short context over the CU, with
+// room for two register chunks per wave.
+template <int D> struct F32Shape;
+template <> struct F32Shape<64> { static constexpr int NW = 8; };
+template <> struct F32Shape<128> { static constexpr int NW = 8; };
+template <> struct F32Shape<256> { static constexpr int NW = 4; };
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
-  constexpr int DPL = D / 64;                    // output dims per lane
-  __shared__ float qs[D];
-  // grid: x = split + S * (head + Hq * token_slot), y = sequence
+struct F32Chunk {
+  f32x4 k[D / 16];                               // K[k0 + l16][16c + 4 q4 .. + 3]
+  float v[D / 16][4];                            // V[k0 + 4 q4 + r][16t + l16]
+};
+
+template <int D, bool WIN>
+__global__ __launch_bounds__(64 * F32Shape<D>::NW) void attn_f32_kernel(const AttnParams p) {
+  constexpr int NW = F32Shape<D>::NW;
+  constexpr int DC = D / 16;                     // 16-dim groups
+  constexpr int ORS = D + 4;                     // merge buffer row stride (floats)
+  __shared__ __attribute__((aligned(16))) float smem[NW * 16 * ORS + 2 * NW * 16];
+
+  // grid: x = split + S * row tile, y = KV head, z = sequence
   const int S = p.num_splits;
-  int x = blockIdx.x;
-  const int split = x % S;
-  x /= S;
-  const int h = x % p.num_q_heads;
-  const int t = x / p.num_q_heads;
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int split = blockIdx.x % S, rt = blockIdx.x / S;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, q4 = lane >> 4;
 
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
-  if (t >= n) return;
+  const int G = p.group;
+  const int r0 = 16 * rt;
+  // tokens past the host bound max_query_len (= p.ws_tok, invalid input) are
+  // not computed: their workspace rows do not exist
+  const int nq = min(n, p.ws_tok);
+  if (nq <= 0 || r0 >= nq * G) return;
+  const int nrows = min(16, nq * G - r0);
+
   const int ps = p.page_size;
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
-  const int kend = p.causal ? clampi(L - n + t + 1, 0, L) : L;
-  const int kpp = p.pages_per_split * ps;
-  // splits cut the pages from the sequence's first window start (page 0
-  // without a window); this row reads only its own window
-  const int k_split = (split_page_base(L, n, p.window, ps) + split * p.pages_per_split) * ps;
-  const int k_begin = p.window > 0 ? max(k_split, L - n + t - p.window + 1) : k_split;
-  const int k_stop = min(k_split + kpp, kend);
-  const int g = h / p.group;
-  const int tok = s0 + t;
+  const int diag = L - n;                        // token t sees keys j <= diag + t
+  const int causal = p.causal;
+  const int t_first = r0 / G, t_last = (r0 + nrows - 1) / G;
+  const int window = WIN ? p.window : 0;
+  // keys some row of the tile may see: [wlo, hi)
+  const int hi = causal ? clampi(diag + t_last + 1, 0, L) : L;
+  const int wlo = WIN && window > 0 ? max(0, diag + t_first - window + 1) : 0;
+  // the split's pages (counted from the sequence's first window start)
+  const int pg0 = split_page_base(L, n, window, ps) + split * p.pages_per_split;
+  const int k_begin = max(pg0 * ps, wlo & ~15);  // 16-key chunks never straddle a page
+  const int k_end = min(min((pg0 + p.pages_per_split) * ps, L), hi);
+  const int nchunks = k_end > k_begin ? (k_end - k_begin + 15) / 16 : 0;
+  // keys below mask_lim are visible to every row, and keys at or above
+  // win_all lie inside every row's window
+  const int mask_lim = min(k_end, causal ? diag + t_first + 1 : L);
+  const int win_all = WIN && window > 0 ? diag + t_last - window + 1 : INT_MIN;
 
-  const float* qp = (const float*)p.q + (int64_t)tok * p.q_stride_tok + (int64_t)h * p.q_stride_head;
-  for (int d = lane; d < D; d += 64) qs[d] = qp[d];
-  __syncthreads();
-
-  const float* kb = (const float*)p.k_pool + (int64_t)g * p.kv_stride_head;
-  const float* vb = (const float*)p.v_pool + (int64_t)g * p.kv_stride_head;
-  float acc[DPL];
+  // ---- Q^T as the B operand: lane (l16, q4) holds Q[row l16][16c + 4 q4 .. + 3]
+  f32x4 qv[DC];
+  const int my_row = r0 + l16;
+  const int my_tok = my_row / G;                 // token of this lane's row
+  if (l16 < nrows) {
+    const float* qp = (const float*)p.q + (int64_t)(s0 + my_tok) * p.q_stride_tok +
+                      (int64_t)(g * G + my_row % G) * p.q_stride_head + 4 * q4;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+    for (int c = 0; c < DC; ++c) qv[c] = *(const f32x4*)(qp + 16 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) qv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  f32x4 acc[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int j0 = k_begin; j0 < k_stop; j0 += 64) {
-    const int j = j0 + lane;
-    float s = kNegInf;
-    int64_t off = 0;
-    if (j < k_stop) {
-      const int lp = j / ps;
-      off = (int64_t)page_of(p, b, lp) * p.kv_stride_page + (int64_t)(j - lp * ps) * p.kv_stride_slot;
-      const f32x4* kr = (const f32x4*)(kb + off);
-      float dot = 0.f;
-#pragma unroll 4
-      for (int d4 = 0; d4 < D / 4; ++d4) {
-        const f32x4 kv = kr[d4];
-        dot = fmaf(qs[4 * d4], kv[0], dot);
-        dot = fmaf(qs[4 * d4 + 1], kv[1], dot);
-        dot = fmaf(qs[4 * d4 + 2], kv[2], dot);
-        dot = fmaf(qs[4 * d4 + 3], kv[3], dot);
-      }
-      s = dot * p.scale_log2;
+  const float* kbase = (const float*)p.k_pool + (int64_t)g * p.kv_stride_head;
+  const float* vbase = (const float*)p.v_pool + (int64_t)g * p.kv_stride_head;
+  auto slot_off = [&](int j) -> int64_t {        // key j of a chunk inside the sequence's pages
+    const int lp = j / ps;
+    return (int64_t)page_of(p, b, lp) * p.kv_stride_page + (int64_t)(j - lp * ps) * p.kv_stride_slot;
+  };
+
+  auto load = [&](int c, F32Chunk<D>& ch) {
+    const int k0 = k_begin + 16 * c;
+    // the chunk lies in one page: its page id is uniform
+    const int64_t pbase = slot_off(k0);
+    const float* kp = kbase + pbase + (int64_t)l16 * p.kv_stride_slot + 4 * q4;
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc) ch.k[cc] = *(const f32x4*)(kp + 16 * cc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float* vp = vbase + pbase + (int64_t)(4 * q4 + r) * p.kv_stride_slot + l16;
+#pragma unroll
+      for (int t = 0; t < DC; ++t) ch.v[t][r] = vp[16 * t];
     }
-    const float cmax = wave_max(s);
+  };
+
+  auto process = [&](int c, const F32Chunk<D>& ch) {
+    const int k0 = k_begin + 16 * c;
+    const bool need_mask = k0 + 16 > mask_lim || k0 < win_all;
+    // S^T = K . Q^T
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st = mfma_f32(ch.k[cc][e], qv[cc][e], st);
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = st[r] * p.scale_log2;
+      if (need_mask) {
+        const int j = k0 + 4 * q4 + r;
+        const bool vis = j < k_end && (!causal || j <= diag + my_tok) &&
+                         (!WIN || window <= 0 || j > diag + my_tok - window);
+        v = vis ? v : kNegInf;
+      }
+      x[r] = v;
+    }
+    float cmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    cmax = fmaxf(cmax, shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, shfl_xor(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);
     const float m_safe = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_safe);
-    const float pj = fast_exp2(s - m_safe);
-    l_run = alpha * l_run + wave_sum(pj);
     m_run = m_new;
+    float pr[4];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] *= alpha;
-    const int cnt = min(64, k_stop - j0);
-    for (int jj = 0; jj < cnt; ++jj) {
-      const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj));
-      const int64_t o = (int64_t)__builtin_amdgcn_readlane((int)(off & 0xffffffff), jj) |
-                        ((int64_t)__builtin_amdgcn_readlane((int)(off >> 32), jj) << 32);
-      const float* vr = vb + o;
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - m_safe);
+    l_run = alpha * l_run + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pw, vr[lane + 64 * i], acc[i]);
+    for (int t = 0; t < DC; ++t) acc[t] *= alpha;
+    // O^T += V^T . P^T; value rows outside [wlo, k_end) are selected to zero
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = k0 + 4 * q4 + r;
+      const bool live = !need_mask || (j < k_end && j >= wlo);
+#pragma unroll
+      for (int t = 0; t < DC; ++t) acc[t] = mfma_f32(live ? ch.v[t][r] : 0.f, pr[r], acc[t]);
+    }
+  };
+
+  // two chunks per wave in registers: chunk c + NW is loaded while c is computed
+  F32Chunk<D> buf[2];
+  if (wave < nchunks) load(wave, buf[0]);
+  for (int base = wave; base < nchunks; base += 2 * NW) {
+    if (base + NW < nchunks) load(base + NW, buf[1]);
+    process(base, buf[0]);
+    if (base + NW < nchunks) {
+      if (base + 2 * NW < nchunks) load(base + 2 * NW, buf[0]);
+      process(base + NW, buf[1]);
     }
   }
 
-  if (p.sinks && split == 0) {
-    // the sink joins split 0 as one more score with no value row
-    const float s2 = p.sinks[h] * kLog2e;
-    const float mn = fmaxf(m_run, s2);
-    const float ms = mn == kNegInf ? 0.f : mn;
-    const float e = fast_exp2(m_run - ms);
-    l_run = l_run * e + fast_exp2(s2 - ms);
+  // ---- merge the waves' states (fixed order: bitwise repeatable)
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  float* Ob = smem;                              // [NW][16][ORS]
+  float* Mw = smem + NW * 16 * ORS;              // [NW][16]
+  float* Lw = Mw + NW * 16;                      // [NW][16]
+  if (q4 == 0) Mw[wave * 16 + l16] = m_run;
+  __syncthreads();
+  {
+    float M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] *= e;
-    m_run = mn;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, Mw[w * 16 + l16]);
+    const float e = fast_exp2(m_run - (M == kNegInf ? 0.f : M));
+    if (q4 == 0) Lw[wave * 16 + l16] = l_run * e;
+    // lane (l16, q4) holds O^T[16t + 4 q4 + r][row l16]
+#pragma unroll
+    for (int t = 0; t < DC; ++t)
+      *(f32x4*)(Ob + (wave * 16 + l16) * ORS + 16 * t + 4 * q4) = acc[t] * e;
   }
+  __syncthreads();
+
   const int64_t NH = (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;   // workspace rows per split
-  if (S == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = (float*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head;
+  for (int it = threadIdx.x; it < nrows * (D / 4); it += 64 * NW) {
+    const int row = it / (D / 4), c4 = it % (D / 4);
+    const int tok = (r0 + row) / G, head = g * G + (r0 + row) % G;
+    float M = kNegInf, Lt = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) op[lane + 64 * i] = acc[i] * inv;
-  } else {
-    const int64_t ri = (int64_t)split * NH + ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) p.ws_acc[ri * D + lane + 64 * i] = acc[i];
-    if (lane == 0) {
-      p.ws_ml[ri * 2] = m_run;
-      p.ws_ml[ri * 2 + 1] = l_run;
+    for (int w = 0; w < NW; ++w) {
+      M = fmaxf(M, Mw[w * 16 + row]);
+      Lt += Lw[w * 16 + row];
+      o += *(const f32x4*)(Ob + (w * 16 + row) * ORS + 4 * c4);
+    }
+    if (p.sinks && split == 0) {
+      // the sink joins split 0 as one more score with no value row
+      const float s2 = p.sinks[head] * kLog2e;
+      const float Mn = fmaxf(M, s2);
+      const float Ms = Mn == kNegInf ? 0.f : Mn;
+      const float e = fast_exp2(M - Ms);
+      Lt = Lt * e + fast_exp2(s2 - Ms);
+      o *= e;
+      M = Mn;
+    }
+    if (S == 1) {
+      const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+      float* op = (float*)p.out + (int64_t)(s0 + tok) * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
+      *(f32x4*)op = o * inv;
+    } else {
+      const int64_t ri = (int64_t)split * NH + ((int64_t)b * p.ws_tok + tok) * p.num_q_heads + head;
+      *(f32x4*)(p.ws_acc + ri * D + 4 * c4) = o;
+      if (c4 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{M, Lt};
     }
   }
 }
 
 template <int D>
-static hipError_t launch_f32_t(const AttnParams& p, int max_q, hipStream_t st) {
-  const int64_t gx = (int64_t)p.num_splits * p.num_q_heads * max_q;
-  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3((unsigned)gx, p.num_seqs), dim3(64), 0, st, p);
+static hipError_t launch_f32_t(const AttnParams& p, hipStream_t st) {
+  const int64_t gx = (int64_t)p.num_splits * p.num_qtiles;
+  const dim3 grid((unsigned)gx, p.num_kv_heads, p.num_seqs), block(64 * F32Shape<D>::NW);
+  if (p.window > 0) hipLaunchKernelGGL((attn_f32_kernel<D, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((attn_f32_kernel<D, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_f32(const AttnParams& p, int max_q, hipStream_t st) {
+// p.num_qtiles: 16-row tiles per sequence (ceil(max_query_len * G / 16)).
+hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
   switch (p.head_dim) {
-    case 64: return launch_f32_t<64>(p, max_q, st);
-    case 128: return launch_f32_t<128>(p, max_q, st);
-    case 256: return launch_f32_t<256>(p, max_q, st);
+    case 64: return launch_f32_t<64>(p, st);
+    case 128: return launch_f32_t<128>(p, st);
+    case 256: return launch_f32_t<256>(p, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -125,6 +125,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int G = p.group;
   const int rows = n * G;
   if (n <= 0 || n > p.dec_max_n || rows <= p.row_lo || rows > p.row_hi) return;
+  // a step longer than the host bound max_query_len (invalid input) would
+  // index split partials past its workspace rows: such a sequence is skipped
+  if (!p.ws_flat && n > p.ws_tok && (p.num_splits > 1 || p.force_partial)) return;
 
   const int ps = p.page_size;
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);

@@ -55,12 +55,14 @@ int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W) {
   if (d->num_splits > 0) return d->num_splits < W ? d->num_splits : W;
   if (cu_count < 1) cu_count = 1;
   // units of parallel work per split: (sequence, KV head) workgroups of 4 waves
-  // for the bf16 decode kernel, (token, query head) waves for float32.
+  // for the bf16 decode kernel; (sequence, KV head, 16-row tile) workgroups of
+  // 4-16 waves for float32, which spread a split's keys over all their waves.
   const int N = d->num_tokens;
   const int mql = d->max_query_len > 0 && d->max_query_len < N ? d->max_query_len : N;
+  const int G = d->num_q_heads / d->num_kv_heads;
   int64_t units = dtype == PA_BF16 ? (int64_t)d->num_seqs * d->num_kv_heads
-                                   : (int64_t)d->num_seqs * d->num_q_heads * (mql > 0 ? mql : 1);
-  int64_t target = dtype == PA_BF16 ? 2 * (int64_t)cu_count : 8 * (int64_t)cu_count;
+                                   : (int64_t)d->num_seqs * d->num_kv_heads * f32_row_tiles(mql, G);
+  int64_t target = dtype == PA_BF16 ? 2 * (int64_t)cu_count : (int64_t)cu_count;
   if (units < 1) units = 1;
   int64_t want = (target + units - 1) / units;
   // A step of one-token decodes that cannot fill two workgroups per CU aims
@@ -68,7 +70,11 @@ int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W) {
   // splits shorten the longest sequence's tail.  Mixed batches measured
   // faster with two.
   if (dtype == PA_BF16 && mql == 1 && units < target) want = (3 * (int64_t)cu_count + units - 1) / units;
-  const int min_pages = (256 + d->page_size - 1) / d->page_size;
+  // at least 256 keys per bf16 split; a float32 split keeps at least 1024 so
+  // each of its waves has chunks to walk (a short context is one launch with
+  // no combine)
+  const int min_keys = dtype == PA_BF16 ? 256 : 1024;
+  const int min_pages = (min_keys + d->page_size - 1) / d->page_size;
   const int64_t cap_pages = (W + min_pages - 1) / min_pages;
   int64_t s = want;
   if (s > 32) s = 32;
@@ -131,6 +137,7 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
     pl.ws_tok = dmax;
   } else {
     pl.dec_max_n = 0;
+    pl.num_qtiles = f32_row_tiles(pl.mql, G);
     pl.splits_big = pl.splits;
     pl.pages_per_split_big = pl.pages_per_split;
     pl.combine = pl.splits > 1 && pl.mql >= 1;

@@ -22,7 +22,7 @@ struct Plan {
   int big_nt;              // 2 or 4 row tiles
   bool prefill;            // bf16: prefill launch for n > dec_max_n
   int tok_per_tile;        // prefill: tokens per tile (tile rows / G)
-  int num_qtiles;          // prefill: tiles per sequence (from mql)
+  int num_qtiles;          // prefill: tiles per sequence (from mql); float32: 16-row tiles
   bool combine;            // split partials need the combine launch
   int comb_tokens;         // combine: token slots per sequence
   int comb_max_n;          // combine: sequences with n <= comb_max_n
@@ -34,9 +34,10 @@ struct Plan {
 // Checks dims and dtype; PA_OK or the error status (nothing else is touched).
 pa_status check_dims(const pa_dims* d, pa_dtype dtype);
 
-// Split count from host scalars only: enough workgroups to fill `cu_count`
-// CUs about twice, at least 256 keys per split, at most 32 splits; an
-// explicit dims->num_splits > 0 wins (capped at W).
+// Split count from host scalars only: bf16 aims at about two workgroups per
+// CU with at least 256 keys per split, float32 at one workgroup per CU with
+// at least 1024 keys per split; at most 32 splits; an explicit
+// dims->num_splits > 0 wins (capped at W).
 int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count);
 // The same rule over W pages instead of the table width.
 int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W);

@@ -14,6 +14,10 @@ constexpr int prefill_tile_rows(int head_dim) { return head_dim <= 128 ? 256 : 1
 // Keys per K/V block of the prefill kernel (also the granule of the
 // cascade's prefix key ranges).
 constexpr int prefill_block_keys() { return 64; }
+// Float32 kernel: 16-row tiles (step tokens x group heads) per sequence.
+constexpr int f32_row_tiles(int max_query_len, int group) {
+  return max_query_len > 0 ? (max_query_len * group + 15) / 16 : 1;
+}
 
 struct AttnParams {
   const void* q;
@@ -38,7 +42,7 @@ struct AttnParams {
   int32_t dec_max_n;        // sequences with n <= dec_max_n are the decode class
   int32_t row_lo, row_hi;   // decode kernel: takes sequences with row_lo < n*G <= row_hi
   int32_t tok_per_tile;     // prefill: query tokens per tile
-  int32_t num_qtiles;       // prefill: tiles per (sequence, KV head)
+  int32_t num_qtiles;       // prefill: tiles per (sequence, KV head); float32: 16-row tiles per sequence
   int32_t comb_max_n;       // combine: sequences with n <= comb_max_n
   int32_t comb_tokens;      // combine: token slots per sequence in the grid
   int32_t comb_splits_small;  // combine: splits of rows with n*G <= 16 (1 = written by the decode kernel)
