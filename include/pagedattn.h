@@ -316,7 +316,7 @@ size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn
  * rows (one token, or n*G <= 16 rows): dims->num_splits when > 0, else enough
  * workgroups for two per CU of the current device (three when every sequence
  * has one token, max_query_len == 1, and two are not reached), with at least
- * 256 keys per split and at most 32 splits (page "32. Production attention
+ * 128 keys per split and at most 64 splits (page "32. Production attention
  * kernels", How many splits?).  Verification blocks (16 < n*G <= 64 rows) use 8 splits
  * unless dims->num_splits is set.  Returns 1 for invalid dims.
  */

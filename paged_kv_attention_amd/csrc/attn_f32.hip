@@ -276,69 +276,91 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
 //   out = sum_s w_s acc_s / sum_s w_s l_s, and zero when the sum is zero.
 // This is the log-sum-exp merge of page "32. Production attention kernels"
 // (Long contexts: split the keys) written for unnormalised partials, as in
-// page "Attention and KV Cache" (Split-KV decode, Combine).  Splits are summed
-// in index order, so the result does not depend on scheduling.
+// page "Attention and KV Cache" (Split-KV decode, Combine).
+// One 256-thread workgroup per row: the threads form 256 / (D/4) groups,
+// group k takes splits k, k + groups, ... (each thread 4 dims), so a row with
+// many splits costs a few memory latencies rather than one per split.  The
+// groups' sums are added in LDS in group order, so the result does not
+// depend on scheduling.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) void combine_kernel(const AttnParams p) {
-  constexpr int DPL = D / 64;
+__global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
+  constexpr int CPR = D / 4;                     // threads per partial row (4 dims each)
+  constexpr int NGR = 256 / CPR;                 // split groups
+  __shared__ float red[NGR][D + 4];
+  __shared__ float red_m[NGR], red_l[NGR];
   const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int grp = threadIdx.x / CPR, c4 = threadIdx.x % CPR;
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
   if (t >= n || n > p.comb_max_n) return;
+  const int tok = s0 + t;
   // rows of the 16-row decode tile and of the verify tile may use different
   // split counts; a class with one split was written by its decode kernel
   const int S = n * p.group <= 16 ? p.comb_splits_small : p.comb_splits_big;
   if (S <= 1) return;
-  const int tok = s0 + t;
+  const float* acc_p = p.ws_acc;
+  const float* ml_p = p.ws_ml;
   // workspace rows per split: (sequence, step token) slots, or flat tokens
   const int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
   const int64_t row = p.ws_flat ? (int64_t)tok * p.num_q_heads + h : ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
-  // Splits are read in groups of 8 whose loads are all issued before any is
-  // used (one memory latency per group and pass rather than one per split);
-  // padding entries (-inf, 0) leave the sums bit for bit unchanged.
+  // this group's maximum, four splits' loads in flight at a time; padding
+  // entries are (-inf, 0) and leave every sum bit for bit unchanged
   float M = kNegInf;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float m[8];
+  for (int s = grp; s < S; s += 4 * NGR) {
+    float m[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = s0 + j < S ? p.ws_ml[((s0 + j) * NH + row) * 2] : kNegInf;
+    for (int j = 0; j < 4; ++j) m[j] = s + j * NGR < S ? ml_p[((s + j * NGR) * NH + row) * 2] : kNegInf;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) M = fmaxf(M, m[j]);
+    for (int j = 0; j < 4; ++j) M = fmaxf(M, m[j]);
   }
+  if (c4 == 0) red_m[grp] = M;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NGR; ++k) M = fmaxf(M, red_m[k]);
   const float Ms = M == kNegInf ? 0.f : M;
-  float acc[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float mv[8], lv[8], av[8][DPL];
+  for (int s = grp; s < S; s += 4 * NGR) {
+    f32x2 ml[4];
+    f32x4 av[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t ri = (s0 + j) * NH + row;
-      const bool in = s0 + j < S;
-      mv[j] = in ? p.ws_ml[ri * 2] : kNegInf;
-      lv[j] = in ? p.ws_ml[ri * 2 + 1] : 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) av[j][i] = in ? p.ws_acc[ri * D + lane * DPL + i] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const int sj = s + j * NGR;
+      if (sj < S) {
+        const int64_t ri = sj * NH + row;
+        ml[j] = *(const f32x2*)(ml_p + ri * 2);
+        av[j] = *(const f32x4*)(acc_p + ri * D + 4 * c4);
+      } else {
+        ml[j] = f32x2{kNegInf, 0.f};
+        av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = fast_exp2(mv[j] - Ms);
-      l = fmaf(w, lv[j], l);
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, av[j][i], acc[i]);
+    for (int j = 0; j < 4; ++j) {
+      const float w = fast_exp2(ml[j][0] - Ms);
+      l = fmaf(w, ml[j][1], l);
+      acc += w * av[j];
     }
+  }
+  *(f32x4*)&red[grp][4 * c4] = acc;
+  if (c4 == 0) red_l[grp] = l;
+  __syncthreads();
+  if (grp != 0) return;
+  acc = *(const f32x4*)&red[0][4 * c4];
+  l = red_l[0];
+#pragma unroll
+  for (int k = 1; k < NGR; ++k) {
+    acc += *(const f32x4*)&red[k][4 * c4];
+    l += red_l[k];
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (BF16) {
-    __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + lane * DPL;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) op[i] = (__bf16)(acc[i] * inv);
+    __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + 4 * c4;
+    *(u32x2*)op = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   } else {
-    float* op = (float*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + lane * DPL;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) op[i] = acc[i] * inv;
+    float* op = (float*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)h * p.o_stride_head + 4 * c4;
+    *(f32x4*)op = acc * inv;
   }
 }
 
@@ -346,9 +368,9 @@ template <int D>
 static hipError_t launch_combine_t(const AttnParams& p, bool bf16, hipStream_t st) {
   dim3 grid(p.num_q_heads, p.comb_tokens, p.num_seqs);
   if (bf16)
-    hipLaunchKernelGGL((combine_kernel<D, true>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((combine_kernel<D, true>), grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((combine_kernel<D, false>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((combine_kernel<D, false>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
