@@ -80,7 +80,7 @@ struct DecodeLds {
   static constexpr int ROWS = 16 * NT;
   static constexpr int ORS = D + 4;              // merge buffer row stride in floats
   static constexpr int STAGE = 4 * DecodeCfg<D, KQ>::WAVE_LDS;
-  static constexpr int MERGE = (8 * ROWS + ROWS * ORS) * 4;
+  static constexpr int MERGE = (128 + ROWS * ORS) * 4;
   static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
 };
 
@@ -99,7 +99,8 @@ struct DecodeChunk {
 // loop).  FW: the launch also writes the step's new rows (bf16 pools, 16-row
 // tiles; see the main loop).
 template <int D, int NT, bool WIN, int KQ, int NB = 0, bool FW = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void decode_splitkv_kernel(const AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 && (WIN || KQ != KV_BF16) ? 1 : 2)))
+void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D, KQ>;
   constexpr bool QUANT = KQ != KV_BF16;
   constexpr int ROWS = 16 * NT;
@@ -119,6 +120,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int b = hf ? blockIdx.y : blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
+  // Row groups: the tile's 16*NT rows form NT groups of 16.  Wave w computes
+  // group rg = w % NT over the chunks c with c % KG == w / NT: the KG = 4/NT
+  // waves of a group split its chunks, and every wave keeps the state of 16
+  // rows only (so a 32- or 64-row tile needs no more registers per wave than
+  // the 16-row one).
+  constexpr int KG = 4 / NT;
+  const int rg = wave % NT, kg = wave / NT;
 
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
@@ -152,10 +160,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int win_all = WIN ? max(key_lo, window > 0 ? diag + n - window : INT_MIN) : INT_MIN;
 
   // ---- query tile as the B operand of S^T = K . Q^T (row = lane % 16)
-  bf16x8 qB[NT][C::DS];
+  bf16x8 qB[1][C::DS];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = 16 * nt + l16;
+  for (int nt = 0; nt < 1; ++nt) {
+    const int r = 16 * (rg + nt) + l16;
     if (r < rows) {
       const int tok = s0 + r / G, head = g * G + r % G;
       const __bf16* qp = (const __bf16*)p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
@@ -186,9 +194,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   // qsum the row sum of the bf16 query and pvsum the row sum of the
   // probabilities the PV product used (rescaled with the accumulator).
   constexpr bool BIAS = KQ == KV_INT8;
-  float qsum[NT], pvsum[NT];
+  float qsum[1], pvsum[1];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < 1; ++nt) {
     float a = 0.f;
     if constexpr (BIAS) {
 #pragma unroll
@@ -202,10 +210,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     pvsum[nt] = 0.f;
   }
 
-  f32x4 acc[NT][C::DT];
-  float m_run[NT], l_run[NT];
+  f32x4 acc[1][C::DT];
+  float m_run[1], l_run[1];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < 1; ++nt) {
     m_run[nt] = kNegInf;
     l_run[nt] = 0.f;
 #pragma unroll
@@ -244,8 +252,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const int t = (i * 64 / C::CPL) / 16;       // uniform per load
       const char* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) * C::EB + 16 * cc;
       // a wave's V load covers whole rows (full cache lines) that no other
-      // workgroup reads: a streaming (nontemporal) load reads them faster
-      ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
+      // workgroup reads: a streaming (nontemporal) load reads them faster.
+      // In a 32- or 64-row tile the waves of the other row groups read the
+      // same rows, from the cache.
+      if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
+      else ch.v[i] = *(const u32x4*)vp;
     }
     if constexpr (QUANT) {
       // lane l: scale of key k0 + l % 32, of K for l < 32 and of V above;
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       }
     }
     // S^T = K . Q^T
-    f32x4 st[2][NT];
+    f32x4 st[2][1];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       bf16x8 kf[C::DS];
@@ -314,18 +325,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
         }
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < 1; ++nt) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) a = mfma16(kf[s], qB[nt][s], a);
         st[t][nt] = a;
       }
     }
-    bf16x8 pB[NT];
+    bf16x8 pB[1];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < 1; ++nt) {
       float x[2][4];
-      const int tok = (16 * nt + l16) / G;
+      const int tok = (16 * (rg + nt) + l16) / G;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -393,12 +404,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const u32x2 a2 = lds_read_tr16(r2 + 32 * dt);
       const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a1.x, a1.y, a2.x, a2.y});
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma16(va, pB[nt], acc[nt][dt]);
+      for (int nt = 0; nt < 1; ++nt) acc[nt][dt] = mfma16(va, pB[nt], acc[nt][dt]);
     }
   };
 
-  // Register pipeline of NBUF chunks per wave: chunk c + 4*(NBUF-1) is loaded
-  // while chunk c is computed.  NBUF = 1 (load a chunk, then compute it) is
+  // Register pipeline of NBUF chunks per wave: chunk c + KG*(NBUF-1) is
+  // loaded while chunk c is computed.  NBUF = 1 (load a chunk, then compute it) is
   // the measured best on the 64 x 4096 decode step: a second chunk in flight
   // per wave (register double buffering, or issuing the next chunk's loads
   // before this chunk's softmax) lowers the achieved HBM bandwidth.  A launch
@@ -434,22 +445,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     }
     __syncthreads();
   }
+  // a row group past the step's rows has nothing to compute (its waves
+  // still take part in the merge)
+  const int my_chunks = 16 * rg < rows ? nchunks : 0;
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j)
-    if (wave + 4 * j < nchunks) load(wave + 4 * j, buf[j]);
-  for (int base = wave; base < nchunks; base += 4 * NBUF) {
+    if (kg + KG * j < my_chunks) load(kg + KG * j, buf[j]);
+  for (int base = kg; base < my_chunks; base += KG * NBUF) {
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) {
-      const int c = base + 4 * k;
-      const int cn = c + 4 * (NBUF - 1);
-      if (cn < nchunks) load(cn, buf[(k + NBUF - 1) % NBUF]);
-      if (c < nchunks) process(c, buf[k]);
+      const int c = base + KG * k;
+      const int cn = c + KG * (NBUF - 1);
+      if (cn < my_chunks) load(cn, buf[(k + NBUF - 1) % NBUF]);
+      if (c < my_chunks) process(c, buf[k]);
     }
   }
 
-  // ---- merge the four waves' states (fixed order: bitwise repeatable)
+  // ---- merge the states of the waves of each row group (fixed order:
+  // bitwise repeatable)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < 1; ++nt) {
     l_run[nt] += shfl_xor(l_run[nt], 16);
     l_run[nt] += shfl_xor(l_run[nt], 32);
     if constexpr (BIAS) {
@@ -462,35 +477,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     }
   }
   __syncthreads();                              // staging tiles are free from here on
-  float* Mw = (float*)smem;                     // [4][ROWS]
-  float* Lw = Mw + 4 * ROWS;                    // [4][ROWS]
-  float* Ob = Lw + 4 * ROWS;                    // [ROWS][ORS]
-  if (q4 == 0) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) Mw[wave * ROWS + 16 * nt + l16] = m_run[nt];
-  }
+  float* Mw = (float*)smem;                     // [4 waves][16 rows of the wave's group]
+  float* Lw = Mw + 64;                          // [4 waves][16]
+  float* Ob = Lw + 64;                          // [ROWS][ORS]
+  if (q4 == 0) Mw[wave * 16 + l16] = m_run[0];
   __syncthreads();
+  {
+    float M = kNegInf;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = 16 * nt + l16;
-    float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
+    for (int k = 0; k < KG; ++k) M = fmaxf(M, Mw[(rg + NT * k) * 16 + l16]);
     const float Ms = M == kNegInf ? 0.f : M;
-    const float e = fast_exp2(m_run[nt] - Ms);
-    l_run[nt] *= e;
+    const float e = fast_exp2(m_run[0] - Ms);
+    l_run[0] *= e;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] *= e;
-    if (q4 == 0) Lw[wave * ROWS + row] = l_run[nt];
+    for (int dt = 0; dt < C::DT; ++dt) acc[0][dt] *= e;
+    if (q4 == 0) Lw[wave * 16 + l16] = l_run[0];
   }
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+  for (int k = 0; k < KG; ++k) {
+    if (kg == k) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          f32x4* o = (f32x4*)(Ob + (16 * nt + l16) * ORS + 16 * dt + 4 * q4);
-          *o = (w == 0) ? acc[nt][dt] : (*o + acc[nt][dt]);
-        }
+      for (int dt = 0; dt < C::DT; ++dt) {
+        f32x4* o = (f32x4*)(Ob + (16 * rg + l16) * ORS + 16 * dt + 4 * q4);
+        *o = (k == 0) ? acc[0][dt] : (*o + acc[0][dt]);
+      }
     }
     __syncthreads();
   }
@@ -501,8 +511,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   for (int it = threadIdx.x; it < nrows * (D / 4); it += 256) {
     const int row = it / (D / 4), c4 = it % (D / 4);
     const int tok = s0 + row / G, head = g * G + row % G;
-    float M = fmaxf(fmaxf(Mw[row], Mw[ROWS + row]), fmaxf(Mw[2 * ROWS + row], Mw[3 * ROWS + row]));
-    float Lt = ((Lw[row] + Lw[ROWS + row]) + Lw[2 * ROWS + row]) + Lw[3 * ROWS + row];
+    // the row's group and the waves that computed it
+    float M = kNegInf, Lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int w = (row >> 4) + NT * k;
+      M = fmaxf(M, Mw[w * 16 + (row & 15)]);
+      Lt += Lw[w * 16 + (row & 15)];
+    }
     f32x4 o = *(const f32x4*)(Ob + row * ORS + 4 * c4);
     if (p.sinks && split == 0) {
       // the sink joins split 0 as one more score with no value row
@@ -604,7 +620,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
           break;
         }
       }
-      if constexpr (NT == 1 && D <= 128) {
+      if constexpr (D <= 128) {
         if (p.num_splits > 1) {
           if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2>), grid, dim3(256), 0, st, p);
           else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 2>), grid, dim3(256), 0, st, p);

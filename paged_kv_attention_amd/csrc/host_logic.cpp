@@ -119,18 +119,23 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
     pl.prefill = pl.mql > pl.dec_max_n;
     pl.tok_per_tile = prefill_tile_rows(d->head_dim) / G;
     pl.num_qtiles = pl.prefill ? (pl.mql + pl.tok_per_tile - 1) / pl.tok_per_tile : 0;
-    // The verify-tile launch (n*G > 16) serves few sequences, so its pages
-    // are cut into 8 splits of >= 256 keys (page "Attention kernels", Decode:
-    // verify steps use 8 splits).
+    // The verify-tile launch (16 < n*G <= 64 rows): about two workgroups per
+    // CU over the batch's (sequence, KV head) pairs, at least 256 keys per
+    // split, at most 64 splits (page "Attention kernels", Decode: verify
+    // steps of one sequence take several splits).
     if (d->num_splits > 0) {
       pl.splits_big = pl.splits;
       pl.pages_per_split_big = pl.pages_per_split;
     } else {
+      const int64_t units = (int64_t)(d->num_seqs > 0 ? d->num_seqs : 1) * d->num_kv_heads;
+      int64_t want = (2 * (int64_t)(cu_count > 0 ? cu_count : 1) + units - 1) / units;
       const int min_pages = (256 + d->page_size - 1) / d->page_size;
-      int ppb = (W + 7) / 8;
-      if (ppb < min_pages) ppb = min_pages;
-      pl.pages_per_split_big = ppb;
-      pl.splits_big = (W + ppb - 1) / ppb;
+      const int64_t cap_pages = (W + min_pages - 1) / min_pages;
+      if (want > 64) want = 64;
+      if (want > cap_pages) want = cap_pages;
+      if (want < 1) want = 1;
+      pl.pages_per_split_big = (int)((W + want - 1) / want);
+      pl.splits_big = (W + pl.pages_per_split_big - 1) / pl.pages_per_split_big;
     }
     if (!pl.dec_big) pl.splits_big = 1;
     pl.combine = dmax >= 1 && ((pl.dec_small && pl.splits > 1) || (pl.dec_big && pl.splits_big > 1));
