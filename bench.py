@@ -213,14 +213,16 @@ class PrefillBench:
 
 
 class WorkloadBench:
-    """Any seeded workload on device, pools rotated over `layers` sets."""
+    """Any seeded workload on device, pools rotated over `layers` sets.
+    `config` is a config number of workloads.make, or a Workload."""
 
-    def __init__(self, config, layers=1, window=0, sinks=False, kv_kind=None):
+    def __init__(self, config, layers=1, window=0, sinks=False, kv_kind=None, num_splits=0):
         import torch
         import paged_kv_attention_amd as pa
         from workloads import make
         self.torch, self.pa = torch, pa
-        self.w = w = make(config)
+        self.w = w = make(config) if isinstance(config, int) else config
+        self.num_splits = num_splits
         self.window = window
         # sink logits: one per query head, drawn from their own seeded stream
         self.sinks_cpu = (torch.randn(w.num_q_heads, generator=torch.Generator().manual_seed(777)) * 2.0
@@ -255,7 +257,8 @@ class WorkloadBench:
             torch.cuda.synchronize()
             self.pools = qpools
         self.out = torch.empty_like(self.q)
-        dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=w.max_query_len)
+        dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=w.max_query_len,
+                            num_splits=num_splits)
         self.ws = torch.empty(max(pa.workspace_size(dims, w.dtype), 16), dtype=torch.uint8, device=dev)
         self.splits = pa.choose_splits(dims)
         lens = w.context_lens.tolist()
@@ -272,39 +275,65 @@ class WorkloadBench:
         w = self.w
         return self.pa.paged_attention(self.q, k, v, self.bt, self.cl, self.qsl, w.scale, w.causal, out=self.out,
                                        workspace=self.ws, max_query_len=w.max_query_len, window=self.window,
-                                       sinks=self.sinks, kv_quant=self.quant[layer % len(self.pools)])
+                                       sinks=self.sinks, kv_quant=self.quant[layer % len(self.pools)],
+                                       num_splits=self.num_splits)
 
+
+
+def _hbm_entry(name, wb, steps, warmup, layers):
+    """Per-call, GPU-side and back-to-back times of one workload and its HBM
+    roofline (algorithmic bytes over the GPU-side time per call)."""
+    import torch
+    _, per = _time_steps([wb.attend], steps, warmup)
+    ms = per[0]
+    gpu = _time_queued(wb.attend, steps, warmup)
+    # calls back to back: two events around all calls and none between
+    # them, so the host's launch path runs ahead of the GPU's work
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        wb.attend(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_b2b = e0.elapsed_time(e1) / steps
+    gbs = wb.bytes / (gpu["median"] * 1e-3) / 1e9
+    return {"workload": name, "ms": round(ms, 5), "gpu_ms": gpu["median"], "gpu_ms_min": gpu["min"],
+            "ms_back_to_back": round(ms_b2b, 5), "splits": wb.splits, "algorithmic_bytes": wb.bytes,
+            "algorithmic_flops": wb.flops, "GB_s": round(gbs, 2), "hbm_frac_per_call": round(wb.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "hbm_frac_back_to_back": round(wb.bytes / (ms_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "time": "gpu_ms (queued)"},
+            "pool_sets_rotated": layers}
 
 
 def other_workloads(steps, warmup):
-    """Latency of the fp32 single-sequence decode, GB/s of the ragged decode
-    batch and of the mixed batch (their HBM-bound rooflines), with pools
-    rotated so the Infinity Cache cannot hold them."""
+    """The other configurations and the decode shapes the headline leaves out:
+    the fp32 single-sequence decode (latency), the ragged decode batch, the
+    mixed batch, one long bf16 sequence at 4096 and 32768 positions (one
+    sequence must still fill the chip), and a batch of 16-token verification
+    steps; each with its HBM roofline.  Pools are rotated so the Infinity
+    Cache cannot hold them.  `ms` brackets each call with events (the host's
+    launch path included); `gpu_ms` is the GPU time per call with the host
+    running ahead (see _time_queued); the roofline uses gpu_ms."""
     import torch
+    from workloads import make_custom
     res = {}
-    for cfg, layers, name in [(1, 1, "fp32 single-sequence decode, 8/2 heads, D 64, page 16, ctx 600"),
-                              (2, 8, "bf16 ragged decode, 32 seqs, ctx U{1..4096}, 32/8 heads, D 128, page 64"),
-                              (4, 8, "bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify")]:
-        print(f"[bench] other workload {cfg}: building inputs", file=sys.stderr, flush=True)
+    one = lambda L, seed: make_custom(seed=seed, context_lens=[L], query_lens=[1], num_q_heads=32, num_kv_heads=8,
+                                      head_dim=128, page_size=64, dtype=torch.bfloat16,
+                                      name=f"bf16 decode of one sequence at {L} positions, 32/8 heads, D 128, page 64")
+    verify = make_custom(seed=13, context_lens=[2048] * 64, query_lens=[16] * 64, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, page_size=64, dtype=torch.bfloat16,
+                         name="bf16 verification: 64 seqs x 16-token steps at 2048 positions, 32/8 heads, D 128, page 64")
+    for key, cfg, layers, name in [
+            ("config1", 1, 1, "fp32 single-sequence decode, 8/2 heads, D 64, page 16, ctx 600"),
+            ("config2", 2, 8, "bf16 ragged decode, 32 seqs, ctx U{1..4096}, 32/8 heads, D 128, page 64"),
+            ("config4", 4, 8, "bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify"),
+            ("decode_1x4096", one(4096, 11), 32, None),
+            ("decode_1x32768", one(32768, 12), 8, None),
+            ("verify_64x16_at_2048", verify, 4, None)]:
+        print(f"[bench] other workload {key}: building inputs", file=sys.stderr, flush=True)
         wb = WorkloadBench(cfg, layers)
-        _, per = _time_steps([wb.attend], steps, warmup)
-        ms = per[0]
-        # calls back to back: two events around all calls and none between
-        # them, so the host's launch path runs ahead of the GPU's work
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            wb.attend(i)
-        e1.record()
-        torch.cuda.synchronize()
-        ms_b2b = e0.elapsed_time(e1) / steps
-        entry = {"workload": name, "ms": round(ms, 5), "ms_back_to_back": round(ms_b2b, 5), "splits": wb.splits,
-                 "algorithmic_bytes": wb.bytes, "GB_s": round(wb.bytes / (ms * 1e-3) / 1e9, 2),
-                 "hbm_frac": round(wb.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "GB_s_back_to_back": round(wb.bytes / (ms_b2b * 1e-3) / 1e9, 2),
-                 "hbm_frac_back_to_back": round(wb.bytes / (ms_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "algorithmic_flops": wb.flops, "pool_sets_rotated": layers}
-        res[f"config{cfg}"] = entry
+        res[key] = _hbm_entry(name or wb.w.name, wb, steps, warmup, layers)
         del wb
         torch.cuda.empty_cache()
     return res
@@ -463,6 +492,40 @@ def _time_steps(step_fns, steps, warmup):
     return total, per
 
 
+_SPIN_CYCLES_PER_MS = None
+
+
+def _time_queued(step_fn, steps, warmup):
+    """GPU time per call with the host running ahead of the GPU: a spin
+    kernel holds the GPU while every call and its pair of events are
+    enqueued, so each pair brackets the call's own GPU work (its launches and
+    the gaps between them) rather than the host's launch path.  Returns the
+    median and minimum in ms."""
+    import torch
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    for i in range(warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # hold the GPU for about 0.2 ms per call to be enqueued (the host needs
+    # well under that per call)
+    torch.cuda._sleep(int(_SPIN_CYCLES_PER_MS * (1.0 + 0.2 * steps)))
+    for i in range(steps):
+        evs[i][0].record()
+        step_fn(warmup + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return _spread([a.elapsed_time(b) for a, b in evs])
+
+
 def _spread(times):
     """Median and minimum of one function's per-step times (ms)."""
     t = sorted(times)
@@ -497,6 +560,17 @@ def read_ceiling(reps=10):
     return round(4 * (1 << 30) / (best * 1e-3) / 1e9, 1)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, seconds_target=12.0):
     """The float64 oracle, as it stands, on a bounded sample of the decode
     workload: whole sequences (all heads) in order, cycling, until about
@@ -519,9 +593,78 @@ def cpu_baseline(w, seconds_target=12.0):
         done_seqs += 1
     el = time.perf_counter() - t_start
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{done_seqs} sequence passes (64 x 4096 decode step, one sequence with all 32 heads "
                       f"per pass), float64, {el:.1f} s"}
+
+
+def cpu_baseline_configs(seconds_per_config=3.0):
+    """The oracle on a bounded sample of every configuration, with the same
+    algorithmic bytes (decode configs, GB/s) or flops (prefill configs,
+    TFLOP/s) as the GPU rows: whole sequences in turn for the decode
+    configurations, the last query rows of sequence 0 (the longest rows of a
+    causal prompt) for the prefills."""
+    import torch
+    from oracle import attention_f64
+    from workloads import make
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    res = {}
+    for cfg in (1, 2, 3, 4, 5, 6):
+        w = make(cfg)
+        qsl = w.query_start_loc.tolist()
+        lens = w.context_lens.tolist()
+        e = 4 if w.dtype == torch.float32 else 2
+        t0 = time.perf_counter()
+        units, done_b, done_f = 0, 0, 0
+        if cfg in (5, 6):
+            rows = 64
+            while time.perf_counter() - t0 < seconds_per_config or units == 0:
+                toks = list(range(qsl[1] - rows * (units + 1), qsl[1] - rows * units))
+                attention_f64(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
+                              tokens=toks)
+                L = lens[0]
+                done_f += sum(4 * w.head_dim * w.num_q_heads * (L - (qsl[1] - t) + 1) for t in toks)
+                units += 1
+            el = time.perf_counter() - t0
+            res[f"config{cfg}"] = {"value": round(done_f / el / 1e12, 6), "unit": "TFLOP/s", "seconds": round(el, 2),
+                                   "sample": f"{units * rows} query tokens (all heads) at the end of sequence 0"}
+        else:
+            while time.perf_counter() - t0 < seconds_per_config or units == 0:
+                b = units % w.num_seqs
+                sub = torch.tensor([0, qsl[b + 1] - qsl[b]], dtype=torch.int32)
+                attention_f64(w.q[qsl[b]:qsl[b + 1]], w.k_pool, w.v_pool, w.block_tables[b:b + 1],
+                              w.context_lens[b:b + 1], sub, w.scale)
+                done_b += algorithmic_bytes([lens[b]], [qsl[b + 1] - qsl[b]], w.num_q_heads, w.num_kv_heads,
+                                            w.head_dim, w.page_size, e)
+                units += 1
+            el = time.perf_counter() - t0
+            res[f"config{cfg}"] = {"value": round(done_b / el / 1e9, 4), "unit": "GB/s", "seconds": round(el, 2),
+                                   "sample": f"{units} sequence passes (all heads)"}
+        del w
+    res["cores"] = torch.get_num_threads()
+    res["cpu_model"] = cpu_model()
+    return res
+
+
+def trace_summary(db_path, drop):
+    """Per-kernel durations from a rocprofv3 results database (kernel
+    trace), in launch order per kernel and grid: all dispatches, and the
+    dispatches after the first `drop` of each (the warm-up launches)."""
+    import re
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = list(con.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x from kernels order by start"))
+    groups = {}
+    for name, dur, gx, gy, gz, wx in rows:
+        short = re.sub(r"\(.*", "", name)
+        groups.setdefault((short, gx // max(wx, 1), gy, gz), []).append(dur / 1000.0)
+    lines = [f"{'kernel':70s} {'grid (workgroups)':>22s} {'n':>4s} {'avg_us':>9s} {'n_timed':>7s} {'avg_timed_us':>12s} {'min_us':>8s}"]
+    for (short, gx, gy, gz), ds in groups.items():
+        timed = ds[drop:] if len(ds) > drop else ds
+        lines.append(f"{short[:70]:70s} {f'({gx},{gy},{gz})':>22s} {len(ds):4d} {sum(ds) / len(ds):9.2f} "
+                     f"{len(timed):7d} {sum(timed) / len(timed):12.2f} {min(ds):8.2f}")
+    return "\n".join(lines)
 
 
 def main():
@@ -536,11 +679,18 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other measured workloads")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay of the decode step")
     ap.add_argument("--no-variants", action="store_true", help="skip the sliding-window / sink workloads")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_d256"], default=None,
                     help="time one workload only (for profiler runs)")
+    ap.add_argument("--trace-summary", metavar="DB", default=None,
+                    help="print per-kernel durations from a rocprofv3 results database and exit")
+    ap.add_argument("--drop", type=int, default=0,
+                    help="with --trace-summary: dispatches of each kernel counted as warm-up")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (scales profiler byte counters)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.drop))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design note, "
               "not a built path.", file=sys.stderr)
@@ -615,9 +765,11 @@ def main():
                                       "how": "library read probe (pa_read_probe): 16-byte streaming loads "
                                              "over a 4 GiB buffer, best of 10"}
 
-    if args.only in (None, "prefill") and not args.no_prefill:
-        print("[bench] prefill: building inputs", file=sys.stderr, flush=True)
-        pb = PrefillBench(5)
+    for leg, cfg in (("prefill", 5), ("prefill_d256", 6)):
+        if args.only not in (None, leg) or args.no_prefill:
+            continue
+        print(f"[bench] {leg}: building inputs", file=sys.stderr, flush=True)
+        pb = PrefillBench(cfg)
         psteps = max(3, min(args.steps, 10))
         pwarm = max(args.warmup, PREFILL_WARMUP)
         total, per = _time_steps([lambda i: pb.write(), lambda i: pb.attend()], psteps, pwarm)
@@ -626,24 +778,26 @@ def main():
         step_ms = total / psteps
         tflops_kernel = pb.flops / (kern_ms * 1e-3) / 1e12
         tflops_step = pb.flops / (step_ms * 1e-3) / 1e12
-        pre = {"workload": "causal prefill 4 x 8192, 32 q / 8 kv heads, head_dim 128, page 64, bf16; "
-                           "kv_cache_write of 32768 tokens + paged_attention",
+        w = pb.w
+        pre = {"workload": f"causal prefill 4 x 8192, {w.num_q_heads} q / {w.num_kv_heads} kv heads, "
+                           f"head_dim {w.head_dim}, page 64, bf16; kv_cache_write of 32768 tokens + paged_attention",
                "steps": psteps, "warmup": pwarm, "ms_per_step": round(step_ms, 4),
                "tflops_step": round(tflops_step, 2),
                "algorithmic_flops": pb.flops,
                "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops_kernel / BF16_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic("prefill"), "kernel": "prefill_kernel<128>",
+                            "traffic": measured_traffic(leg) if leg in TRAFFIC_FILES else None,
+                            "kernel": f"prefill_kernel<{w.head_dim}>",
                             "kernel_ms": round(kern_ms, 4), "kernel_ms_median": kern_spread["median"],
                             "kernel_ms_min": kern_spread["min"]}}
-        if args.only == "prefill":
+        if args.only == leg:
             result.update({"metric": METRIC, "value": round(tflops_kernel, 2), "unit": "TFLOP/s", "n_gpus": 1,
                            "steps": psteps, "warmup": pwarm, "ms_per_step": round(step_ms, 4),
                            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                            "data": "synthetic", "config": {"workload": pre["workload"]},
                            "roofline": pre["roofline"]})
         else:
-            result["prefill"] = pre
+            result[leg] = pre
         del pb
         torch.cuda.empty_cache()
 
@@ -658,6 +812,8 @@ def main():
     if not args.no_cpu_baseline and args.only is None and decode_w is not None:
         print("[bench] cpu baseline: timing the float64 oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(decode_w)
+        print("[bench] cpu baseline: the oracle on every configuration", file=sys.stderr, flush=True)
+        result["cpu_baseline_configs"] = cpu_baseline_configs()
     print(json.dumps(result), flush=True)
 
 
