@@ -44,7 +44,11 @@ CSRC = os.path.join(ROOT, "paged_kv_attention_amd", "csrc")
 # a plain copy's counts) is kept next to the hash of the sources it was taken
 # from; a kernel changed since then reports traffic null.
 TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.json"), "decode.hip"),
-                 "prefill": (os.path.join(ROOT, "profiles", "prefill_c5_traffic.json"), "prefill.hip")}
+                 "prefill": (os.path.join(ROOT, "profiles", "prefill_c5_traffic.json"), "prefill.hip"),
+                 "prefill_d256": (os.path.join(ROOT, "profiles", "prefill_c6_traffic.json"), "prefill.hip")}
+# kernel (name prefix and head-dim template argument) each traffic file is about
+TRAFFIC_KERNELS = {"decode": "pa::decode_splitkv_kernel<128, 1,", "prefill": "pa::prefill_kernel<128,",
+                   "prefill_d256": "pa::prefill_kernel<256,"}
 
 
 # ----------------------------------------------------------------------------- accounting
@@ -647,14 +651,122 @@ def cpu_baseline_configs(seconds_per_config=3.0):
     return res
 
 
-def trace_summary(db_path, drop):
-    """Per-kernel durations from a rocprofv3 results database (kernel
-    trace), in launch order per kernel and grid: all dispatches, and the
-    dispatches after the first `drop` of each (the warm-up launches)."""
+def _counter_rows(path, counter):
+    """(dispatch id, kernel name, value) of one counter from a rocprofv3
+    counter_collection CSV, in dispatch order."""
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
+
+
+def traffic_summary(which, fetch_csv, write_csv):
+    """HBM bytes per launch of the kernel `which` stands for, from a
+    FETCH_SIZE and a WRITE_SIZE counter run (KiB per dispatch) of
+    `bench.py --only ... --copy-calibration`: each counter is scaled by what
+    it reads for the 1 GiB calibration copy (the runtime's copy kernel), then
+    compared with the algorithmic bytes of one launch.
+    Writes the traffic JSON the bench reads and returns the text summary."""
+    from workloads import make
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    kname = TRAFFIC_KERNELS[which]
+    # the calibration is the 1 GiB device-to-device copy (the runtime's copy
+    # kernel); the fill that prepares its source writes as much but reads
+    # nothing
+    cal_w = max((r for r in write if "copyBuffer" in r[1]), key=lambda r: r[2])
+    cal_f = max((r for r in fetch if "copyBuffer" in r[1]), key=lambda r: r[2])
+    cal_name = cal_w[1]
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = gib_kib / cal_f[2], gib_kib / cal_w[2]
+    fk = [r[2] for r in fetch if r[1].startswith(kname) or ("void " + kname) in r[1]]
+    wk = [r[2] for r in write if r[1].startswith(kname) or ("void " + kname) in r[1]]
+    fb = sum(fk) / len(fk) * 1024 * f_scale
+    wb = sum(wk) / len(wk) * 1024 * w_scale
+    cfg = {"decode": 3, "prefill": 5, "prefill_d256": 6}[which]
+    w = make(cfg)
+    alg = algorithmic_bytes(w.context_lens.tolist(), w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                            w.page_size, 2)
+    src = TRAFFIC_FILES[which][1]
+    rec = {"kernel": kname, "workload": w.name, "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
+           "write_bytes": int(round(wb)), "algorithmic_bytes": alg, "src_sha256_16": kernel_src_hash(src),
+           "source": os.path.relpath(TRAFFIC_FILES[which][0].replace("_traffic.json", "_hbm_traffic.txt"), ROOT)}
+    with open(TRAFFIC_FILES[which][0], "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"copy calibration ({cal_name[:40]}): FETCH_SIZE {cal_f[2]:.1f} KiB, WRITE_SIZE {cal_w[2]:.1f} KiB for 1 GiB",
+             f"scale factors: fetch {f_scale:.4f}, write {w_scale:.4f} (bytes per counter byte)",
+             f"FETCH_SIZE per dispatch (KiB): {[round(x, 1) for x in fk]}",
+             f"WRITE_SIZE per dispatch (KiB): {[round(x, 1) for x in wk]}",
+             f"scaled traffic per launch: fetch {int(fb)} B + write {int(wb)} B = {int(fb + wb)} B",
+             f"algorithmic bytes per launch: {alg} B -> traffic / algorithmic = {(fb + wb) / alg:.4f}",
+             f"source hash ({src} + pa_device.h + pa_params.h, sha256[:16]): {rec['src_sha256_16']}"]
+    return "\n".join(lines)
+
+
+def counter_summary(csv_paths, kernel, drop):
+    """Average counter values per dispatch of `kernel` (a name prefix) over
+    rocprofv3 counter_collection CSVs, after the first `drop` dispatches, and
+    the figures derived from them: the clock the kernel ran at, MFMA busy
+    per SIMD, VALU / LDS / transcendental instructions per MFMA, and the L2
+    hit rate.  MI355X: 8 XCDs, 256 CUs, 4 SIMDs per CU."""
+    import csv
+    vals, times = {}, {}
+    for path in csv_paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if not (r["Kernel_Name"].startswith(kernel) or ("void " + kernel) in r["Kernel_Name"]):
+                    continue
+                d = int(r["Dispatch_Id"])
+                vals.setdefault(r["Counter_Name"], {})[d] = float(r["Counter_Value"])
+                times[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    avg = {}
+    for name, per in vals.items():
+        ds = sorted(per)[drop:] or sorted(per)
+        avg[name] = sum(per[d] for d in ds) / len(ds)
+    ds = sorted(times)[drop:] or sorted(times)
+    t_ns = sum(times[d] for d in ds) / len(ds)
+    lines = [f"{k:28s} {v:12.4g}" for k, v in sorted(avg.items())]
+    lines.append(f"kernel time per dispatch (counter run): {t_ns / 1000:.1f} us over {len(ds)} dispatches")
+    if "GRBM_GUI_ACTIVE" in avg:
+        clk = avg["GRBM_GUI_ACTIVE"] / 8 / t_ns
+        lines.append(f"clock over the kernel, GRBM_GUI_ACTIVE / 8 XCDs / time: {clk:.3f} GHz")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            lines.append(f"MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8) = "
+                         f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (avg['GRBM_GUI_ACTIVE'] / 8):.3f}")
+    if "SQ_INSTS_MFMA" in avg and avg["SQ_INSTS_MFMA"] > 0:
+        m = avg["SQ_INSTS_MFMA"]
+        parts = [f"MFMA instructions per SIMD: {m / 1024:.0f}"]
+        for k, label in (("SQ_INSTS_VALU", "VALU (incl. MFMA)"), ("SQ_INSTS_VALU_TRANS_F32", "exp2"),
+                         ("SQ_INSTS_LDS", "LDS")):
+            if k in avg:
+                parts.append(f"{label} per MFMA: {avg[k] / m:.2f}")
+        lines.append("; ".join(parts))
+    if "SQ_WAVE_CYCLES" in avg and "SQ_WAIT_INST_LDS" in avg:
+        lines.append(f"SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES: {avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f}")
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+        lines.append(f"L2 hit rate: {avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.3f}")
+    return "\n".join(lines)
+
+
+def trace_summary(path, drop):
+    """Per-kernel durations from a rocprofv3 kernel trace (a results
+    database, or the kernel_trace CSV of --output-format csv), in launch order
+    per kernel and grid: all dispatches, and the dispatches after the first
+    `drop` of each (the warm-up launches)."""
+    import csv
     import re
     import sqlite3
-    con = sqlite3.connect(db_path)
-    rows = list(con.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x from kernels order by start"))
+    if path.endswith(".csv"):
+        with open(path) as f:
+            rows = [(r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), int(r["Grid_Size_X"]),
+                     int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]), int(r["Workgroup_Size_X"]))
+                    for r in csv.DictReader(f)]
+    else:
+        con = sqlite3.connect(path)
+        rows = list(con.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x from kernels order by start"))
     groups = {}
     for name, dur, gx, gy, gz, wx in rows:
         short = re.sub(r"\(.*", "", name)
@@ -685,11 +797,23 @@ def main():
                     help="print per-kernel durations from a rocprofv3 results database and exit")
     ap.add_argument("--drop", type=int, default=0,
                     help="with --trace-summary: dispatches of each kernel counted as warm-up")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="decode|prefill|prefill_d256 and the FETCH_SIZE / WRITE_SIZE counter CSVs of a "
+                         "--copy-calibration run: write the traffic JSON under profiles/ and print the summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG", default=None,
+                    help="KERNEL_PREFIX CSV [CSV ...]: average counters of that kernel (after --drop dispatches) "
+                         "over counter_collection CSVs and print the derived figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (scales profiler byte counters)")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.drop))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(*args.traffic_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary[1:], args.counter_summary[0], args.drop))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design note, "
