@@ -86,9 +86,11 @@ struct DecodeLds {
 
 template <int D, int KQ>
 struct DecodeChunk {
-  // K: 8 dims of one key per (tile, k-step): bf16x8, or 8 codes
-  using KReg = typename std::conditional<KQ == KV_BF16, bf16x8, u32x2>::type;
-  KReg k[2][DecodeCfg<D, KQ>::DS];
+  // K: bf16 pools, 8 dims of one key per (tile, k-step); 1-byte codes, 16
+  // dims of one key per (tile, pair of k-steps), one 16-byte load each
+  static constexpr int KN = KQ == KV_BF16 ? DecodeCfg<D, KQ>::DS : DecodeCfg<D, KQ>::DS / 2;
+  using KReg = typename std::conditional<KQ == KV_BF16, bf16x8, u32x4>::type;
+  KReg k[2][KN];
   u32x4 v[DecodeCfg<D, KQ>::VLOADS];
   float sc;                                      // quantized: scale of key lane%32, K (lane<32) or V
 };
@@ -160,6 +162,13 @@ void decode_splitkv_kernel(const AttnParams p) {
   const int win_all = WIN ? max(key_lo, window > 0 ? diag + n - window : INT_MIN) : INT_MIN;
 
   // ---- query tile as the B operand of S^T = K . Q^T (row = lane % 16)
+  // In k-step s lane (l16, q4) holds dims kdim(s) .. kdim(s) + 7 of its key
+  // (A operand) and of its query row (B operand): 32 s + 8 q4 for bf16 pools;
+  // for 1-byte codes 64 (s / 2) + 16 q4 + 8 (s % 2), so that the two k-steps
+  // 2j, 2j + 1 of a lane take one 16-byte piece of the key row.  Any
+  // assignment of dims to k slots that K and Q share gives the same dot
+  // product.
+  auto kdim = [&](int s) { return QUANT ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1) : 32 * s + 8 * q4; };
   bf16x8 qB[1][C::DS];
 #pragma unroll
   for (int nt = 0; nt < 1; ++nt) {
@@ -168,14 +177,14 @@ void decode_splitkv_kernel(const AttnParams p) {
       const int tok = s0 + r / G, head = g * G + r % G;
       const __bf16* qp = (const __bf16*)p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) qB[nt][s] = *(const bf16x8*)(qp + 32 * s + 8 * q4);
+      for (int s = 0; s < C::DS; ++s) qB[nt][s] = *(const bf16x8*)(qp + kdim(s));
       if (QUANT && p.k_smooth) {
         // scaling q per channel by the key smoothing cancels it in q . k
         const float* sm = p.k_smooth + (int64_t)g * D;
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) {
-          const f32x4 a = *(const f32x4*)(sm + 32 * s + 8 * q4);
-          const f32x4 b = *(const f32x4*)(sm + 32 * s + 8 * q4 + 4);
+          const f32x4 a = *(const f32x4*)(sm + kdim(s));
+          const f32x4 b = *(const f32x4*)(sm + kdim(s) + 4);
           const bf16x8 v = qB[nt][s];
           qB[nt][s] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2((float)v[0] * a[0], (float)v[1] * a[1]),
                                                        pack_bf16x2((float)v[2] * a[2], (float)v[3] * a[3]),
@@ -241,9 +250,15 @@ void decode_splitkv_kernel(const AttnParams p) {
     const int k0 = k_begin + c * C::KC;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const char* kp = kbase + (tile_off(k0 + 16 * t, l16) + 8 * q4) * C::EB;
+      if constexpr (QUANT) {
+        const char* kp = kbase + tile_off(k0 + 16 * t, l16) + 16 * q4;
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const typename DecodeChunk<D, KQ>::KReg*)(kp + 32 * s * C::EB);
+        for (int j = 0; j < C::DS / 2; ++j) ch.k[t][j] = *(const u32x4*)(kp + 64 * j);
+      } else {
+        const char* kp = kbase + (tile_off(k0 + 16 * t, l16) + 8 * q4) * C::EB;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const bf16x8*)(kp + 32 * s * C::EB);
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::VLOADS; ++i) {
@@ -314,11 +329,11 @@ void decode_splitkv_kernel(const AttnParams p) {
       bf16x8 kf[C::DS];
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) {
-        if constexpr (BIAS) {
-          const u32x2 a = i8x4_to_bf16_biased(ch.k[t][s].x), b2 = i8x4_to_bf16_biased(ch.k[t][s].y);
-          kf[s] = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b2.x, b2.y});
-        } else if constexpr (QUANT) {
-          const u32x2 a = codes4_to_bf16<KQ>(ch.k[t][s].x), b2 = codes4_to_bf16<KQ>(ch.k[t][s].y);
+        if constexpr (QUANT) {
+          const u32x4& w = ch.k[t][s >> 1];
+          const uint32_t w0 = (s & 1) ? w.z : w.x, w1 = (s & 1) ? w.w : w.y;
+          const u32x2 a = BIAS ? i8x4_to_bf16_biased(w0) : codes4_to_bf16<KQ>(w0);
+          const u32x2 b2 = BIAS ? i8x4_to_bf16_biased(w1) : codes4_to_bf16<KQ>(w1);
           kf[s] = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b2.x, b2.y});
         } else {
           kf[s] = ch.k[t][s];
