@@ -179,6 +179,26 @@ def _stream_ptr(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+# Dims structs (and their plain workspace sizes) of recent call shapes: a
+# serving loop repeats a few shapes, and building the struct field by field
+# is most of the binding's host time.  The cached struct is never modified.
+_DIMS_CACHE: dict = {}
+
+
+def _cached_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor, out: torch.Tensor,
+                 max_query_len: Optional[int], num_splits: int):
+    key = (q.shape, q.stride(), q.dtype, k_pool.shape, k_pool.stride(), block_tables.shape, out.stride(),
+           max_query_len, num_splits)
+    hit = _DIMS_CACHE.get(key)
+    if hit is None:
+        d = make_dims(q, k_pool, block_tables, out=out, max_query_len=max_query_len, num_splits=num_splits)
+        need = int(load_library().pa_workspace_size(ctypes.byref(d), _dtype_code(q.dtype)))
+        if len(_DIMS_CACHE) >= 256:
+            _DIMS_CACHE.clear()
+        hit = _DIMS_CACHE[key] = (d, need)
+    return hit
+
+
 def make_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor, *, out: Optional[torch.Tensor] = None,
               max_query_len: Optional[int] = None, num_splits: int = 0) -> PaDims:
     if q.dim() != 3 or k_pool.dim() != 4:
@@ -280,7 +300,7 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
         raise TypeError("q and the pools must share one dtype")
     if out is None:
         out = torch.empty_like(q)
-    dims = make_dims(q, k_pool, block_tables, out=out, max_query_len=max_query_len, num_splits=num_splits)
+    dims, need_plain = _cached_dims(q, k_pool, block_tables, out, max_query_len, num_splits)
     bt = _i32(block_tables, "block_tables")
     cl = _i32(context_lens, "context_lens")
     qsl = _i32(query_start_loc, "query_start_loc")
@@ -311,7 +331,7 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
             opts.new_stride_tok, opts.new_stride_head = k_new.stride(0), k_new.stride(1)
         need = int(lib.pa_workspace_size_opts(ctypes.byref(dims), code, ctypes.byref(opts)))
     else:
-        need = int(lib.pa_workspace_size(ctypes.byref(dims), code))
+        need = need_plain
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

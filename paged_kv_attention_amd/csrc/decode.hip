@@ -122,14 +122,6 @@ void decode_splitkv_kernel(const AttnParams p) {
   const int b = hf ? blockIdx.y : blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
-  // Row groups: the tile's 16*NT rows form NT groups of 16.  Wave w computes
-  // group rg = w % NT over the chunks c with c % KG == w / NT: the KG = 4/NT
-  // waves of a group split its chunks, and every wave keeps the state of 16
-  // rows only (so a 32- or 64-row tile needs no more registers per wave than
-  // the 16-row one).
-  constexpr int KG = 4 / NT;
-  const int rg = wave % NT, kg = wave / NT;
-
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
   const int G = p.group;
@@ -138,6 +130,16 @@ void decode_splitkv_kernel(const AttnParams p) {
   // a step longer than the host bound max_query_len (invalid input) would
   // index split partials past its workspace rows: such a sequence is skipped
   if (!p.ws_flat && n > p.ws_tok && (p.num_splits > 1 || p.force_partial)) return;
+
+  // Row groups: the step's rows form groups of 16, NG of them in use (the
+  // tile's NT, or for a 64-row tile whose step fills at most 32 rows, 2).
+  // Wave w computes group rg = w % NG over the chunks c with c % KG == w / NG:
+  // the KG = 4/NG waves of a group split its chunks, and every wave keeps the
+  // state of 16 rows only (so a 32- or 64-row tile needs no more registers
+  // per wave than the 16-row one, and no wave of a partly filled tile idles).
+  const int NG = NT == 4 && rows <= 32 ? 2 : NT;
+  const int KG = 4 / NG;
+  const int rg = wave % NG, kg = wave / NG;
 
   const int ps = p.page_size;
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
@@ -500,7 +502,7 @@ void decode_splitkv_kernel(const AttnParams p) {
   {
     float M = kNegInf;
 #pragma unroll
-    for (int k = 0; k < KG; ++k) M = fmaxf(M, Mw[(rg + NT * k) * 16 + l16]);
+    for (int k = 0; k < KG; ++k) M = fmaxf(M, Mw[(rg + NG * k) * 16 + l16]);
     const float Ms = M == kNegInf ? 0.f : M;
     const float e = fast_exp2(m_run[0] - Ms);
     l_run[0] *= e;
@@ -530,7 +532,7 @@ void decode_splitkv_kernel(const AttnParams p) {
     float M = kNegInf, Lt = 0.f;
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-      const int w = (row >> 4) + NT * k;
+      const int w = (row >> 4) + NG * k;
       M = fmaxf(M, Mw[w * 16 + (row & 15)]);
       Lt += Lw[w * 16 + (row & 15)];
     }
@@ -550,29 +552,21 @@ void decode_splitkv_kernel(const AttnParams p) {
       // this row (flat workspace rows) with the suffix state and normalise
       const int64_t NHf = (int64_t)p.num_tokens * p.num_q_heads;
       const int64_t rrow = (int64_t)tok * p.num_q_heads + head;
-      // Partials are read in groups of 8 whose loads are all issued before
-      // any is used: one memory latency per group and pass, not one per
-      // split.  Padding entries (-inf, 0) leave every sum unchanged.
+      // All of a row's partials (up to 16) are loaded before any is used:
+      // one memory latency for the fold.  More partials are read in groups
+      // of 8 whose loads are issued together, one latency per group and
+      // pass.  Padding entries (-inf, 0) leave every sum unchanged, so both
+      // forms add the same terms in the same order.
       const int np = p.merge_prefix;
-      float Mx = M;
-      for (int g0 = 0; g0 < np; g0 += 8) {
-        float m[8];
+      float Ltot;
+      f32x4 ot;
+      if (np <= 16) {
+        f32x2 ml[16];
+        f32x4 pa[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m[j] = g0 + j < np ? p.ws_ml[((g0 + j) * NHf + rrow) * 2] : kNegInf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, m[j]);
-      }
-      const float Ms = Mx == kNegInf ? 0.f : Mx;
-      const float e0 = fast_exp2(M - Ms);
-      float Ltot = Lt * e0;
-      f32x4 ot = o * e0;
-      for (int g0 = 0; g0 < np; g0 += 8) {
-        f32x2 ml[8];
-        f32x4 pa[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (g0 + j < np) {
-            const int64_t ri = (g0 + j) * NHf + rrow;
+        for (int j = 0; j < 16; ++j) {
+          if (j < np) {
+            const int64_t ri = j * NHf + rrow;
             ml[j] = *(const f32x2*)(p.ws_ml + ri * 2);
             pa[j] = *(const f32x4*)(p.ws_acc + ri * D + 4 * c4);
           } else {
@@ -580,11 +574,52 @@ void decode_splitkv_kernel(const AttnParams p) {
             pa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
         }
+        float Mx = M;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) Mx = fmaxf(Mx, ml[j][0]);
+        const float Ms = Mx == kNegInf ? 0.f : Mx;
+        const float e0 = fast_exp2(M - Ms);
+        Ltot = Lt * e0;
+        ot = o * e0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
           const float w = fast_exp2(ml[j][0] - Ms);
           Ltot = fmaf(w, ml[j][1], Ltot);
           ot += w * pa[j];
+        }
+      } else {
+        float Mx = M;
+        for (int g0 = 0; g0 < np; g0 += 8) {
+          float m[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m[j] = g0 + j < np ? p.ws_ml[((g0 + j) * NHf + rrow) * 2] : kNegInf;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, m[j]);
+        }
+        const float Ms = Mx == kNegInf ? 0.f : Mx;
+        const float e0 = fast_exp2(M - Ms);
+        Ltot = Lt * e0;
+        ot = o * e0;
+        for (int g0 = 0; g0 < np; g0 += 8) {
+          f32x2 ml[8];
+          f32x4 pa[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (g0 + j < np) {
+              const int64_t ri = (g0 + j) * NHf + rrow;
+              ml[j] = *(const f32x2*)(p.ws_ml + ri * 2);
+              pa[j] = *(const f32x4*)(p.ws_acc + ri * D + 4 * c4);
+            } else {
+              ml[j] = f32x2{kNegInf, 0.f};
+              pa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float w = fast_exp2(ml[j][0] - Ms);
+            Ltot = fmaf(w, ml[j][1], Ltot);
+            ot += w * pa[j];
+          }
         }
       }
       const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
