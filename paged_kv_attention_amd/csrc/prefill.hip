@@ -426,8 +426,23 @@ void prefill_kernel(const AttnParams p) {
       const float m_upd = need ? m_blk : m_run;
       const float alpha = need ? fast_exp2(m_run - m_blk) : 1.f;   // 0 from -inf
       l_run *= alpha;
+      if constexpr (D == 256) {
+        // The accumulators live in AGPRs here: each is scaled in place by an
+        // AGPR -> VGPR -> AGPR round trip inside this (rare) branch, so the
+        // block loop never holds VGPR copies of them.
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = acc[dt][r], t;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\ts_nop 1\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(t) : "v"(alpha));
+            acc[dt][r] = x;
+          }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+      }
       m_run = m_upd;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
