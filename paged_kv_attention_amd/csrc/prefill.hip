@@ -17,7 +17,8 @@
 // chunks XOR-swizzled by key so the fragment reads stay conflict free.
 // Otherwise blocks pass through a two-stage ring of padded rows, and each
 // thread holds up to PF further blocks in registers (quantized pools are
-// dequantized on the way).
+// dequantized on the way).  256-dim heads over bf16 pools run
+// prefill16_kernel (waves of 16 rows) instead.
 // Per block and wave:
 //   S^T[64 keys x 32 rows] = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS);
 //   mask only blocks that reach the diagonal or the context end (page
@@ -106,8 +107,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
 void prefill_kernel(const AttnParams p) {
   using C = PrefillCfg<D, NW, PF, KB>;
   // direct global -> LDS staging (see above)
-  constexpr bool DMA = KQ == KV_BF16 && (D == 128 || D == 256);
-  constexpr int ROWB = D * 2, BLKB = KB * ROWB, DSTAGE = 2 * BLKB, DNS = D == 128 ? 4 : 2;
+  constexpr bool DMA = KQ == KV_BF16 && D == 128;   // 256-dim bf16 heads run prefill16_kernel
+  constexpr int ROWB = D * 2, BLKB = KB * ROWB, DSTAGE = 2 * BLKB, DNS = 4;
   constexpr int KPI = 1024 / ROWB;               // keys per 1 KiB DMA instruction
   constexpr int CPR = ROWB / 16;                 // 16-byte chunks per key row
   constexpr int LDS_BYTES = DMA ? DNS * DSTAGE : C::LDS;
@@ -304,24 +305,7 @@ void prefill_kernel(const AttnParams p) {
   // S^T = K . Q^T for the 32-key tiles of block blk (raw scores)
   auto qk = [&](int blk, f32x16 (&st)[C::KT]) {
     const PA_LDS char* kl_ = lds + (blk % C::NSTAGE) * C::STAGE;
-    if constexpr (DMA && C::DS > 8) {
-      // key row k holds global chunk c at position c ^ (k & 15); 256-dim
-      // rows: fragments read just before their MFMA
-      const PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt) {
-        f32x16 a;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a[r] = 0.f;
-        const int key = 32 * kt + l32;
-#pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          const bf16x8 ka = *(const PA_LDS bf16x8*)(kd + key * ROWB + 16 * ((2 * s + h2) ^ (key & 15)));
-          a = mfma32(ka, qB[s], a);
-        }
-        st[kt] = a;
-      }
-    } else if constexpr (DMA) {
+    if constexpr (DMA) {
       // key row k holds global chunk c at position c ^ (k & 15)
       const PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
       // the first tile's fragments are requested up front; the second tile's
@@ -673,6 +657,9 @@ static_assert(32 * PrefillShape<256>::NW == prefill_tile_rows(256), "host and ke
 static_assert(PrefillShape<64>::KB == prefill_block_keys() && PrefillShape<128>::KB == prefill_block_keys() &&
               PrefillShape<256>::KB == prefill_block_keys(), "host and kernel block keys differ");
 
+hipError_t launch_prefill16(const AttnParams& p, hipStream_t st);
+hipError_t launch_prefix16(const AttnParams& p, hipStream_t st);
+
 template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
   constexpr int NW = PrefillShape<D>::NW, PF = PrefillShape<D>::PF, KB = PrefillShape<D>::KB;
@@ -689,8 +676,13 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
       else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_FP8>), grid, block, 0, st, p);
       break;
     default:
-      if (win) hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true, KV_BF16>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16>), grid, block, 0, st, p);
+      // 256-dim heads over bf16 pools: the 16-row-wave kernel
+      if constexpr (D == 256) {
+        return launch_prefill16(p, st);
+      } else {
+        if (win) hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, true, KV_BF16>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16>), grid, block, 0, st, p);
+      }
   }
   return hipGetLastError();
 }
@@ -703,7 +695,12 @@ static hipError_t launch_prefix_t(const AttnParams& p, hipStream_t st) {
   switch (p.kv_code) {
     case KV_INT8: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_INT8, true>), grid, block, 0, st, p); break;
     case KV_FP8: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_FP8, true>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16, true>), grid, block, 0, st, p);
+    default:
+      if constexpr (D == 256) {
+        return launch_prefix16(p, st);
+      } else {
+        hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16, true>), grid, block, 0, st, p);
+      }
   }
   return hipGetLastError();
 }
