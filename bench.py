@@ -45,10 +45,10 @@ CSRC = os.path.join(ROOT, "paged_kv_attention_amd", "csrc")
 # from; a kernel changed since then reports traffic null.
 TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.json"), "decode.hip"),
                  "prefill": (os.path.join(ROOT, "profiles", "prefill_c5_traffic.json"), "prefill.hip"),
-                 "prefill_d256": (os.path.join(ROOT, "profiles", "prefill_c6_traffic.json"), "prefill.hip")}
-# kernel (name prefix and head-dim template argument) each traffic file is about
+                 "prefill_d256": (os.path.join(ROOT, "profiles", "prefill_c6_traffic.json"), "prefill16.hip")}
+# kernel (name prefix, with its head-dim template argument) each traffic file is about
 TRAFFIC_KERNELS = {"decode": "pa::decode_splitkv_kernel<128, 1,", "prefill": "pa::prefill_kernel<128,",
-                   "prefill_d256": "pa::prefill_kernel<256,"}
+                   "prefill_d256": "pa::prefill16_kernel<false, false>"}
 
 
 # ----------------------------------------------------------------------------- accounting
@@ -911,7 +911,7 @@ def main():
                "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops_kernel / BF16_PEAK_TFLOPS, 4),
                             "traffic": measured_traffic(leg) if leg in TRAFFIC_FILES else None,
-                            "kernel": f"prefill_kernel<{w.head_dim}>",
+                            "kernel": "prefill16_kernel<256>" if w.head_dim == 256 else f"prefill_kernel<{w.head_dim}>",
                             "kernel_ms": round(kern_ms, 4), "kernel_ms_median": kern_spread["median"],
                             "kernel_ms_min": kern_spread["min"]}}
         if args.only == leg:
