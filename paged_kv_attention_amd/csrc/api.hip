@@ -13,6 +13,16 @@ namespace pa {
 hipError_t launch_decode(const AttnParams& p, int nt, hipStream_t st);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t st);
 hipError_t launch_prefix(const AttnParams& p, hipStream_t st);
+hipError_t launch_verify16(const AttnParams& p, hipStream_t st);
+bool verify16_supported(int head_dim);
+
+// Verification tiles (16 < n*G <= 64 rows): over bf16 pools with 128- or
+// 256-dim heads the shared-block tile of prefill16.hip, otherwise the decode
+// kernel's 32- and 64-row tiles.
+static hipError_t launch_verify(const AttnParams& p, int big_nt, hipStream_t st) {
+  if (p.kv_code == KV_BF16 && verify16_supported(p.head_dim)) return launch_verify16(p, st);
+  return launch_decode(p, big_nt, st);
+}
 hipError_t launch_f32(const AttnParams& p, hipStream_t st);
 hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
@@ -387,7 +397,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
       if (e == hipSuccess && p_side) p_fork = (e = hipStreamWaitEvent(ss->side[0], ss->fork, 0)) == hipSuccess;
       if (e == hipSuccess && v_side) v_fork = (e = hipStreamWaitEvent(ss->side[1], ss->fork, 0)) == hipSuccess;
       if (e == hipSuccess && p_side) e = launch_prefill(p, ss->side[0]);
-      if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, v_side ? ss->side[1] : s);
+      if (e == hipSuccess && pl.dec_big) e = launch_verify(q2, pl.big_nt, v_side ? ss->side[1] : s);
       if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
       if (v_fork) {                          // joined even after a failed launch
         hipError_t j = hipEventRecord(ss->join[1], ss->side[1]);
@@ -413,7 +423,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
       q1.new_stride_head = wp.new_stride_head;
     }
     if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
-    if (e == hipSuccess && pl.dec_big) e = launch_decode(q2, pl.big_nt, s);
+    if (e == hipSuccess && pl.dec_big) e = launch_verify(q2, pl.big_nt, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

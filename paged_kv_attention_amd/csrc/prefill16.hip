@@ -1,16 +1,27 @@
-// Prefill-chunk attention for 256-dim heads over bf16 pools, with waves of
-// 16 query rows on v_mfma_f32_16x16x32_bf16 (gfx950).
-//
-// The tile is the one the host plans for 256-dim heads (128 GQA-packed rows
-// of one sequence and KV head g, row r = token t0 + r / G, query head
-// g*G + r % G; page "Attention kernels", Open questions: GQA packing in the
-// prefill kernel), walked in 64-key blocks that go from global memory
-// straight into LDS (global_load_lds) through a two-stage ring, as in the
-// 32-row kernel.  Here the tile has 8 waves of 16 rows instead of 4 of 32: a
-// wave's accumulators (O^T: 256 dims x 16 rows, 64 registers), query
-// fragments (32) and scores (16) fit two waves per SIMD, so one wave's
-// softmax and LDS waits overlap the other's matrix work.  Each wave reads
-// the whole K and V block from LDS for its 16 rows.
+// GQA-packed attention tiles over bf16 pools with waves of 16 query rows on
+// v_mfma_f32_16x16x32_bf16 (gfx950), K/V blocks shared by the waves through
+// LDS.  Three uses (MODE):
+//   PREFILL  256-dim heads: the tile the host plans (128 rows of one sequence
+//            and KV head g, row r = token t0 + r / G, query head g*G + r % G;
+//            page "Attention kernels", Open questions: GQA packing in the
+//            prefill kernel) in 8 waves.  A wave's accumulators (O^T: 256
+//            dims x 16 rows, 64 registers), query fragments (32) and scores
+//            (16) fit two waves per SIMD, so one wave's softmax and LDS waits
+//            overlap the other's matrix work.
+//   CASCADE  the cascade's prefix pass for 256-dim heads: every query token
+//            of the batch as one flat non-causal sequence over one key range
+//            of the shared prefix; the unnormalised state goes to the split
+//            workspace.
+//   VERIFY   verification steps (page "Attention kernels", Decode: verify
+//            blocks of several tokens): the 16*NW rows of one (sequence, KV
+//            head) against one key range (split) of its pages, 4 waves; the
+//            tile reads each K/V block once from HBM into LDS and all row
+//            groups use it (the decode tile gives every row group its own
+//            copy).  One split writes the normalised rows, several write
+//            partials for the combine, as the decode tiles do.
+// Blocks of 64 keys go from global memory straight into LDS (global_load_lds)
+// through a two-stage ring; each wave reads the whole K and V block from LDS
+// for its 16 rows.
 // Per block and wave:
 //   S^T[64 keys x 16 rows] = K . Q^T (four 16-key tiles, eight 32-dim
 //   k-steps; K row k holds global 16-byte chunk c at position c ^ (k & 15));
@@ -27,9 +38,10 @@
 //   is exactly the B operand of a 32-key k-step whose slot 8 q4 + e stands
 //   for key 32j + 4 q4 + e (e < 4) or 32j + 16 + 4 q4 + e - 4; the V reads
 //   use the same slot-to-key map.
-// With a sliding window and attention sinks, and as the cascade's prefix
-// pass, the tile behaves as in the 32-row kernel (page "32. Production
-// attention kernels", the unified kernel's window mask, Stretch exercises).
+// A sliding window and attention sinks behave as in the 32-row kernel (page
+// "32. Production attention kernels", the unified kernel's window mask,
+// Stretch exercises); in a verification tile with several splits the sink
+// joins split 0's partial.
 #include <limits.h>
 
 #include "pa_device.h"
@@ -52,12 +64,15 @@ __device__ __forceinline__ float xor16_sum(float v) {
 // flight, the other counters not waited on
 constexpr int vm_wait16(int n) { return 0x3f70 | (n & 0xf) | ((n >> 4) << 14); }
 
-template <bool WIN, bool CAS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+enum Tile16Mode { T16_PREFILL = 0, T16_CASCADE = 1, T16_VERIFY = 2 };
+
+template <int D, int NW, bool WIN, int MODE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill16_kernel(const AttnParams p) {
-  constexpr int D = 256, NW = 8, NTH = 64 * NW, KB = 64;
+  constexpr bool CAS = MODE == T16_CASCADE, VER = MODE == T16_VERIFY;
+  constexpr int NTH = 64 * NW, KB = 64;
   constexpr int ROWB = D * 2;                    // bytes per key row
-  constexpr int BLKB = KB * ROWB;                // one tensor's block (32 KiB)
+  constexpr int BLKB = KB * ROWB;                // one tensor's block
   constexpr int DSTAGE = 2 * BLKB;               // K and V of a block
   constexpr int DNS = 2;                         // ring stages
   constexpr int KPI = 1024 / ROWB;               // keys per 1 KiB DMA instruction
@@ -67,12 +82,17 @@ void prefill16_kernel(const AttnParams p) {
   constexpr int DT = D / 16;                     // 16-dim output tiles of PV
   constexpr int KT = KB / 16;                    // 16-key tiles of S^T
   constexpr float TAU = 8.f;                     // lazy-rescale threshold (log2 units)
-  static_assert(16 * NW == prefill_tile_rows(D), "host and kernel tile rows differ");
+  static_assert(VER || 16 * NW == prefill_tile_rows(D), "host and kernel tile rows differ");
   static_assert(prefill_block_keys() % KB == 0, "host blocks are whole kernel blocks");
+  static_assert(DL >= 1 && ROWB <= 1024, "a DMA instruction covers whole key rows");
   __shared__ __attribute__((aligned(1024))) char smem[DNS * DSTAGE];
 
-  int b, g, qt, split = 0;
-  if constexpr (CAS) {
+  int b, g, qt = 0, split = 0;
+  if constexpr (VER) {
+    split = blockIdx.x;                         // split fastest, as the decode tiles
+    g = blockIdx.y;
+    b = blockIdx.z;
+  } else if constexpr (CAS) {
     const int id = blockIdx.x;
     split = id % p.prefix_splits;
     const int rest = id / p.prefix_splits;
@@ -95,26 +115,51 @@ void prefill16_kernel(const AttnParams p) {
 
   const int s0 = CAS ? 0 : p.query_start_loc[b];
   const int n = CAS ? p.num_tokens : p.query_start_loc[b + 1] - s0;
-  if (!CAS && n <= p.dec_max_n) return;         // decode class (or empty)
   const int G = p.group;
-  const int TPT = p.tok_per_tile;
+  if constexpr (VER) {
+    // the verification class of this launch; a step longer than the host
+    // bound max_query_len (invalid input) would index split partials past
+    // its workspace rows and is skipped
+    if (n <= 0 || n > p.dec_max_n || n * G <= p.row_lo || n * G > p.row_hi) return;
+    if (!p.ws_flat && n > p.ws_tok && (p.num_splits > 1 || p.force_partial)) return;
+  } else if constexpr (!CAS) {
+    if (n <= p.dec_max_n) return;               // decode class (or empty)
+  }
+  const int TPT = VER ? n : p.tok_per_tile;
   const int t0 = qt * TPT;
   if (t0 >= n) return;
   const int tcount = min(TPT, n - t0);
   const int rows_valid = tcount * G;
 
+  // Keys [lo, KE) are this tile's range (keys outside it are masked and
+  // never loaded); L is the context length the causal diagonal refers to.
   const int ps = p.page_size, psh = p.page_shift;
-  const int k_lo = CAS ? split * p.prefix_split_keys : 0;
-  const int L = CAS ? min(k_lo + p.prefix_split_keys, p.prefix_len)
-                    : clampi(p.context_lens[b], 0, p.table_width * ps);
+  const int window = WIN ? p.window : 0;
+  int L, lo, KE;
+  if constexpr (CAS) {
+    lo = split * p.prefix_split_keys;
+    L = KE = min(lo + p.prefix_split_keys, p.prefix_len);
+  } else {
+    L = clampi(p.context_lens[b], 0, p.table_width * ps);
+    const int wlo = WIN ? max(0, L - n + t0 - window + 1) : 0;   // the first row's window start
+    if constexpr (VER) {
+      // the split's pages, counted from the first window start (decode tiles' split rule)
+      const int npages = (L + ps - 1) / ps;
+      const int pg0 = wlo / ps + split * p.pages_per_split;
+      const int pg1 = min(pg0 + p.pages_per_split, npages);
+      lo = max(pg0 * ps, wlo);
+      KE = min(pg1 * ps, L);
+    } else {
+      lo = wlo;
+      KE = L;
+    }
+  }
   const int causal = CAS ? 0 : p.causal;
   const int diag = L - n;
-  const int k_hi = causal ? clampi(diag + t0 + tcount, 0, L) : L;   // keys any row can see
-  const int full_lim = causal ? clampi(diag + t0 + 1, 0, L) : L;    // keys every row sees
-  const int nblk = (k_hi + KB - 1) / KB;
-  const int window = WIN ? p.window : 0;
-  const int wlo_tile = WIN ? max(0, diag + t0 - window + 1) : (CAS ? k_lo : 0);
-  const int blk0 = wlo_tile / KB;
+  const int k_hi = min(KE, causal ? clampi(diag + t0 + tcount, 0, L) : L);      // keys any row can see
+  const int full_lim = min(KE, causal ? clampi(diag + t0 + 1, 0, L) : L);       // keys every row sees
+  const int nblk = lo < k_hi ? (k_hi + KB - 1) / KB : 0;
+  const int blk0 = lo / KB;
   const int win_all = WIN ? diag + t0 + tcount - window : INT_MIN;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -157,11 +202,10 @@ void prefill16_kernel(const AttnParams p) {
   // fills LDS bytes [(NW i + w) KiB, +1 KiB) of the K or V block: keys
   // KPI (NW i + w) .. +KPI-1, lane l writing position l % CPR of key
   // KPI (NW i + w) + l / CPR with the global chunk that the swizzle puts
-  // there.  A key outside [lo, L) loads the nearest key inside: a finite copy
+  // there.  A key outside [lo, KE) loads the nearest key inside: a finite copy
   // of a live row whose score is masked and whose probability is 0.
   const int lkey = lane / CPR, lpos = lane % CPR;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int lo = wlo_tile;
   const int64_t lofs = (int64_t)lkey * p.kv_stride_slot;
   auto lane_k = [&](int i) {
     return (uint32_t)((lofs + 8 * (lpos ^ ((KPI * (NW * i + wv) + lkey) & 15))) * 2);   // bytes
@@ -174,7 +218,7 @@ void prefill16_kernel(const AttnParams p) {
   auto page_raw = [&](int blk) { return bt[min((blk * KB) >> psh, p.table_width - 1)]; };
   auto dma = [&](int blk, int pgraw) {
     PA_LDS char* kd = lds + (blk % DNS) * DSTAGE;
-    if (blk * KB >= lo && blk * KB + KB <= L && ps >= KB) {
+    if (blk * KB >= lo && blk * KB + KB <= KE && ps >= KB) {
       // the whole block lies in one page
       const int kb = blk * KB;
       const int lp = kb >> psh;
@@ -192,8 +236,8 @@ void prefill16_kernel(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < DL; ++i) {
         const int kw = blk * KB + KPI * (NW * i + wv);
-        const int jw = clampi(kw, lo, L - 1);
-        const int j = clampi(kw + lkey, lo, L - 1);
+        const int jw = clampi(kw, lo, KE - 1);
+        const int j = clampi(kw + lkey, lo, KE - 1);
         const int key = KPI * (NW * i + wv) + lkey;
         // j and jw share a KPI-key group (or are equal), hence a page
         const int lp = jw >> psh;
@@ -206,7 +250,7 @@ void prefill16_kernel(const AttnParams p) {
       }
     }
   };
-  static_assert(2 * (DNS - 1) * DL < 16, "the blocks in flight fit the wait count");
+  static_assert(2 * (DNS - 1) * DL < 64, "the blocks in flight fit the wait count");
 
   // ---- S^T = K . Q^T for the 16-key tiles of block blk
   f32x4 st[KT];
@@ -227,13 +271,14 @@ void prefill16_kernel(const AttnParams p) {
   // masked maximum of block blk over the row (lanes l16, l16 + 16, + 32, + 48)
   auto block_max = [&](int blk) -> float {
     const int kb0 = blk * KB;
-    if (kb0 + KB > full_lim || kb0 < win_all) {
+    if (kb0 + KB > full_lim || kb0 < win_all || kb0 < lo) {
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = kb0 + 16 * t + 4 * q4 + r;
-          const bool vis = j < L && (!causal || j <= diag + my_tok) && (!WIN || j > diag + my_tok - window);
+          const bool vis = j >= lo && j < KE && (!causal || j <= diag + my_tok) &&
+                           (!WIN || j > diag + my_tok - window);
           st[t][r] = vis ? st[t][r] : kNegInf;
         }
     }
@@ -334,8 +379,10 @@ void prefill16_kernel(const AttnParams p) {
     }
     return;
   }
-  if (p.sinks) {
-    // the row's sink is one more score with no value row
+  const bool partial = VER && (p.num_splits > 1 || p.force_partial);
+  if (p.sinks && (!partial || split == 0)) {
+    // the row's sink is one more score with no value row (in split 0's state
+    // when the splits are merged later)
     const float s2 = row_ok ? p.sinks[my_head] * kLog2e : kNegInf;
     const float mn = fmaxf(m_run, s2);
     const float ms = mn == kNegInf ? 0.f : mn;
@@ -343,6 +390,23 @@ void prefill16_kernel(const AttnParams p) {
     l_run = l_run * e + fast_exp2(s2 - ms);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] *= e;
+    m_run = mn;
+  }
+  if (partial) {
+    // the split's unnormalised state (m in log2 units) at the decode tiles'
+    // workspace row of (sequence, step token, head), or of the flat token
+    if (row_ok) {
+      const int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads
+                                   : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
+      const int64_t rrow = p.ws_flat ? (int64_t)(s0 + my_tok) * p.num_q_heads + my_head
+                                     : ((int64_t)b * p.ws_tok + my_tok) * p.num_q_heads + my_head;
+      const int64_t ri = (int64_t)(p.split_base + split) * NH + rrow;
+      float* wa = p.ws_acc + ri * D + 4 * q4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *(f32x4*)(wa + 16 * dt) = acc[dt];
+      if (q4 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{m_run, l_run};
+    }
+    return;
   }
   if (row_ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -359,15 +423,37 @@ void prefill16_kernel(const AttnParams p) {
 // pass over the flat token range (p.num_qtiles counts its tiles).
 hipError_t launch_prefill16(const AttnParams& p, hipStream_t st) {
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs;
-  if (p.window > 0) hipLaunchKernelGGL((prefill16_kernel<true, false>), dim3((unsigned)total), dim3(512), 0, st, p);
-  else hipLaunchKernelGGL((prefill16_kernel<false, false>), dim3((unsigned)total), dim3(512), 0, st, p);
+  if (p.window > 0)
+    hipLaunchKernelGGL((prefill16_kernel<256, 8, true, T16_PREFILL>), dim3((unsigned)total), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((prefill16_kernel<256, 8, false, T16_PREFILL>), dim3((unsigned)total), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefix16(const AttnParams& p, hipStream_t st) {
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.prefix_splits;
-  hipLaunchKernelGGL((prefill16_kernel<false, true>), dim3((unsigned)total), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((prefill16_kernel<256, 8, false, T16_CASCADE>), dim3((unsigned)total), dim3(512), 0, st, p);
   return hipGetLastError();
+}
+
+// Verification tiles of up to 64 rows over bf16 pools (128- and 256-dim
+// heads): grid (splits, KV heads, sequences) as the decode tiles'.
+bool verify16_supported(int head_dim) { return head_dim == 128 || head_dim == 256; }
+
+template <int D>
+static hipError_t launch_verify16_t(const AttnParams& p, hipStream_t st) {
+  const dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
+  if (p.window > 0) hipLaunchKernelGGL((prefill16_kernel<D, 4, true, T16_VERIFY>), grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((prefill16_kernel<D, 4, false, T16_VERIFY>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify16(const AttnParams& p, hipStream_t st) {
+  switch (p.head_dim) {
+    case 128: return launch_verify16_t<128>(p, st);
+    case 256: return launch_verify16_t<256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pa

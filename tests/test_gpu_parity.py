@@ -99,12 +99,25 @@ def test_bf16_group3_and_mha():
 # (128, 16/32) and (256, 32): blocks span several pages (one page id per
 # 4- or 2-key group); (128, 64/128) and (256, 64/128): one page per block
 @pytest.mark.parametrize("D,ps", [(128, 64), (64, 16), (256, 32), (128, 128), (128, 16), (128, 32), (256, 64),
-                                  (256, 128)])
+                                  (256, 128), (256, 16)])
 def test_bf16_prefill(D, ps):
     lens = [300, 700, 129]
     qlens = [300, 200, 17]
     w = poison_unused(_custom(80 + D + ps, lens, qlens, Hq=8, Hkv=2, D=D, ps=ps))
     check(w, run_lib(w), label=f"bf16 prefill D={D} ps={ps}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (16, 2), (4, 4)])
+def test_bf16_prefill_d256_groups(Hq, Hkv):
+    # 256-dim tiles hold 128 rows: 42 tokens of a 3-head group (126 rows), 16
+    # tokens of an 8-head group, 128 tokens of MHA; ragged tails and a
+    # non-causal sequence
+    lens = [300, 190, 77]
+    qlens = [300, 130, 77]
+    w = poison_unused(_custom(95 + Hq, lens, qlens, Hq=Hq, Hkv=Hkv, D=256, ps=64))
+    check(w, run_lib(w), label=f"bf16 prefill D=256 Hq={Hq} Hkv={Hkv}")
+    w = _custom(96 + Hq, [150, 64], [150, 40], Hq=Hq, Hkv=Hkv, D=256, ps=32, causal=False)
+    check(w, run_lib(w), label=f"bf16 prefill D=256 non-causal Hq={Hq}")
 
 
 def test_bf16_prefill_not_causal_and_group3():
