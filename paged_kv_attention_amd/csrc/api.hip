@@ -330,6 +330,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
     pre.prefix_splits = cp.prefix_splits;
     pre.prefix_split_keys = cp.prefix_split_keys;
     pre.num_qtiles = cp.prefix_qtiles;
+    pre.tok_per_tile = cp.prefix_tile_tokens;
     pre.sinks = nullptr;                       // folded once, by the suffix pass
     AttnParams suf = p;
     suf.key_lo = prefix_len;

@@ -179,14 +179,19 @@ CascadePlan make_cascade_plan(const pa_dims* d, pa_dtype dtype, int cu_count, in
     return c;
   }
   if (cu_count < 1) cu_count = 1;
-  const int tpt = prefill_tile_rows(d->head_dim) / G;
+  // 128- and 256-dim heads: tiles of 64 rows (4 waves of 16), otherwise
+  // the prefill tile
+  const bool t16 = d->head_dim == 128 || d->head_dim == 256;
+  const int tpt = t16 ? 64 / G : prefill_tile_rows(d->head_dim) / G;
+  c.prefix_tile_tokens = tpt;
   c.prefix_qtiles = (N + tpt - 1) / tpt;
   const int kb = prefill_block_keys();
   const int blocks = (prefix_len + kb - 1) / kb;
-  // about half the CUs busy with prefix tiles: more ranges would add more
-  // partial-state traffic than they save in MFMA time
+  // key ranges: about one 64-row tile per CU (half the CUs for the 256-row
+  // tiles); more ranges add more partial-state traffic than they save
   const int64_t units = (int64_t)c.prefix_qtiles * d->num_kv_heads;
-  int64_t s = ((int64_t)cu_count / 2 + units - 1) / units;
+  const int64_t target = t16 ? (int64_t)cu_count : (int64_t)cu_count / 2;
+  int64_t s = (target + units - 1) / units;
   if (s > blocks) s = blocks;
   if (s < 1) s = 1;
   const int per = (int)((blocks + s - 1) / s);

@@ -59,6 +59,7 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window = 0);
 struct CascadePlan {
   pa_status status;
   int prefix_splits, prefix_split_keys, prefix_qtiles;
+  int prefix_tile_tokens;  // query tokens per prefix tile
   int suffix_splits, suffix_pages_per_split;
   size_t workspace_bytes;  // (prefix_splits + suffix_splits) * N * Hq * (D + 2) * 4
 };

@@ -696,7 +696,8 @@ static hipError_t launch_prefix_t(const AttnParams& p, hipStream_t st) {
     case KV_INT8: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_INT8, true>), grid, block, 0, st, p); break;
     case KV_FP8: hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_FP8, true>), grid, block, 0, st, p); break;
     default:
-      if constexpr (D == 256) {
+      // 128- and 256-dim heads over bf16 pools: 64-row tiles of prefill16.hip
+      if constexpr (D == 128 || D == 256) {
         return launch_prefix16(p, st);
       } else {
         hipLaunchKernelGGL((prefill_kernel<D, NW, PF, KB, false, KV_BF16, true>), grid, block, 0, st, p);

@@ -82,7 +82,7 @@ void prefill16_kernel(const AttnParams p) {
   constexpr int DT = D / 16;                     // 16-dim output tiles of PV
   constexpr int KT = KB / 16;                    // 16-key tiles of S^T
   constexpr float TAU = 8.f;                     // lazy-rescale threshold (log2 units)
-  static_assert(VER || 16 * NW == prefill_tile_rows(D), "host and kernel tile rows differ");
+  static_assert(MODE != T16_PREFILL || 16 * NW == prefill_tile_rows(D), "host and kernel tile rows differ");
   static_assert(prefill_block_keys() % KB == 0, "host blocks are whole kernel blocks");
   static_assert(DL >= 1 && ROWB <= 1024, "a DMA instruction covers whole key rows");
   __shared__ __attribute__((aligned(1024))) char smem[DNS * DSTAGE];
@@ -419,8 +419,7 @@ void prefill16_kernel(const AttnParams p) {
   }
 }
 
-// 256-dim heads over bf16 pools: the prefill tiles, and the cascade's prefix
-// pass over the flat token range (p.num_qtiles counts its tiles).
+// 256-dim heads over bf16 pools: the prefill tiles.
 hipError_t launch_prefill16(const AttnParams& p, hipStream_t st) {
   const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs;
   if (p.window > 0)
@@ -430,9 +429,13 @@ hipError_t launch_prefill16(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The cascade's prefix pass over 64-row tiles of the flat token range
+// (128- and 256-dim heads; p.num_qtiles counts the tiles).
 hipError_t launch_prefix16(const AttnParams& p, hipStream_t st) {
-  const int64_t total = (int64_t)p.num_qtiles * p.num_kv_heads * p.prefix_splits;
-  hipLaunchKernelGGL((prefill16_kernel<256, 8, false, T16_CASCADE>), dim3((unsigned)total), dim3(512), 0, st, p);
+  const dim3 grid((unsigned)((int64_t)p.num_qtiles * p.num_kv_heads * p.prefix_splits));
+  if (p.head_dim == 128) hipLaunchKernelGGL((prefill16_kernel<128, 4, false, T16_CASCADE>), grid, dim3(256), 0, st, p);
+  else if (p.head_dim == 256) hipLaunchKernelGGL((prefill16_kernel<256, 4, false, T16_CASCADE>), grid, dim3(256), 0, st, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

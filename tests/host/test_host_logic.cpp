@@ -49,9 +49,15 @@ int main() {
   // cascade: 64 decodes over a 4096-position shared prefix, suffixes up to 8 pages
   pa_dims cc = dims(64, 64, 1, 32, 8, 128, 64, 362, 72);
   pa::CascadePlan cpl = pa::make_cascade_plan(&cc, PA_BF16, 256, 4096, 0);
-  CHECK(cpl.status == PA_OK && cpl.prefix_qtiles == 1 && cpl.prefix_splits == 16 && cpl.prefix_split_keys == 256);
+  // 64-row prefix tiles: 16 tokens of 4 heads, 4 tiles x 8 KV heads, 8 key ranges (one tile per CU)
+  CHECK(cpl.status == PA_OK && cpl.prefix_tile_tokens == 16 && cpl.prefix_qtiles == 4 && cpl.prefix_splits == 8 &&
+        cpl.prefix_split_keys == 512);
   CHECK(cpl.suffix_splits == 1 && cpl.suffix_pages_per_split == 8);
-  CHECK(cpl.workspace_bytes == (size_t)17 * 64 * 32 * 130 * 4);
+  CHECK(cpl.workspace_bytes == (size_t)9 * 64 * 32 * 130 * 4);
+  // 64-dim heads keep the 256-row prefill tiles, about half the CUs busy
+  pa_dims c64 = dims(64, 64, 1, 32, 8, 64, 64, 362, 72);
+  pa::CascadePlan cp64 = pa::make_cascade_plan(&c64, PA_BF16, 256, 4096, 0);
+  CHECK(cp64.status == PA_OK && cp64.prefix_tile_tokens == 64 && cp64.prefix_qtiles == 1 && cp64.prefix_splits == 16);
   CHECK(pa::make_cascade_plan(&cc, PA_BF16, 256, 4000, 0).status == PA_ERR_SHAPE);       // not whole pages
   CHECK(pa::make_cascade_plan(&cc, PA_BF16, 256, 4096, 512).status == PA_ERR_UNSUPPORTED);   // with a window
   CHECK(pa::make_cascade_plan(&cc, PA_F32, 256, 4096, 0).status == PA_ERR_UNSUPPORTED);
