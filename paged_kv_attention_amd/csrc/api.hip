@@ -14,6 +14,7 @@ hipError_t launch_decode(const AttnParams& p, int nt, hipStream_t st);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t st);
 hipError_t launch_prefix(const AttnParams& p, hipStream_t st);
 hipError_t launch_verify16(const AttnParams& p, hipStream_t st);
+hipError_t launch_prefill16_small(const AttnParams& p, hipStream_t st);
 bool verify16_supported(int head_dim);
 
 // Verification tiles (16 < n*G <= 64 rows): over bf16 pools with 128- or
@@ -373,6 +374,17 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
     q2.num_splits = pl.splits_big;
     q2.pages_per_split = pl.pages_per_split_big;
     const int classes = (int)pl.prefill + (int)pl.dec_small + (int)pl.dec_big;
+    // prefill tiles: 64-row tiles spread over the chip for a short prefill
+    // over bf16 pools, the planned tiles otherwise
+    auto run_prefill = [&](hipStream_t st) -> hipError_t {
+      if (!kq && prefill_small_tiles(dims, cu_count())) {
+        AttnParams pp = p;
+        pp.tok_per_tile = 64 / p.group;
+        pp.num_qtiles = (pl.mql + pp.tok_per_tile - 1) / pp.tok_per_tile;
+        return launch_prefill16_small(pp, st);
+      }
+      return launch_prefill(p, st);
+    };
     // New rows: a batch of 16-row decode tiles alone writes them inside its
     // decode launch (each workgroup the rows of its own KV head and pages,
     // before it reads a key); otherwise they are written first.
@@ -397,7 +409,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
       bool p_fork = false, v_fork = false;   // side streams that joined this call
       if (e == hipSuccess && p_side) p_fork = (e = hipStreamWaitEvent(ss->side[0], ss->fork, 0)) == hipSuccess;
       if (e == hipSuccess && v_side) v_fork = (e = hipStreamWaitEvent(ss->side[1], ss->fork, 0)) == hipSuccess;
-      if (e == hipSuccess && p_side) e = launch_prefill(p, ss->side[0]);
+      if (e == hipSuccess && p_side) e = run_prefill(ss->side[0]);
       if (e == hipSuccess && pl.dec_big) e = launch_verify(q2, pl.big_nt, v_side ? ss->side[1] : s);
       if (e == hipSuccess && pl.dec_small) e = launch_decode(q1, 1, s);
       if (v_fork) {                          // joined even after a failed launch
@@ -414,7 +426,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
       ss->mu.unlock();
       return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
-    if (pl.prefill) e = launch_prefill(p, s);
+    if (pl.prefill) e = run_prefill(s);
     q1.head_first = classes == 1;            // decode tiles have the chip to themselves
     if (fuse) {
       q1.new_k = wp.k_new;

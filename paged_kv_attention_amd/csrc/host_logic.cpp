@@ -207,6 +207,15 @@ CascadePlan make_cascade_plan(const pa_dims* d, pa_dtype dtype, int cu_count, in
   return c;
 }
 
+bool prefill_small_tiles(const pa_dims* d, int cu_count) {
+  if (d->head_dim != 128 || d->num_kv_heads < 1) return false;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G < 1 || G > 64) return false;             // a 64-row tile holds at least one token
+  const int64_t rows = (int64_t)d->num_tokens * G;
+  const int64_t tiles = (rows + prefill_tile_rows(128) - 1) / prefill_tile_rows(128) * d->num_kv_heads;
+  return 2 * tiles < (int64_t)cu_count;
+}
+
 pa_status validate_shared_prefix(const int32_t* bt, const int32_t* lens, const int32_t* qsl, int prefix_len,
                                  const pa_dims* d) {
   if (prefix_len <= 0) return PA_OK;

@@ -65,6 +65,11 @@ struct CascadePlan {
 };
 CascadePlan make_cascade_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int prefix_len, int window);
 
+// Whether a batch's prefill tiles run as 64-row tiles (bf16 pools, 128-dim
+// heads): when even the bound N*G on its prefill rows fills fewer 256-row
+// tiles than half the CUs, the smaller tiles spread the work over the chip.
+bool prefill_small_tiles(const pa_dims* d, int cu_count);
+
 // Shared-prefix contract on copied metadata: table rows agree with row 0 on
 // the prefix's pages and every query token sits after the prefix.
 pa_status validate_shared_prefix(const int32_t* block_tables, const int32_t* context_lens,

@@ -82,7 +82,7 @@ void prefill16_kernel(const AttnParams p) {
   constexpr int DT = D / 16;                     // 16-dim output tiles of PV
   constexpr int KT = KB / 16;                    // 16-key tiles of S^T
   constexpr float TAU = 8.f;                     // lazy-rescale threshold (log2 units)
-  static_assert(MODE != T16_PREFILL || 16 * NW == prefill_tile_rows(D), "host and kernel tile rows differ");
+  static_assert(MODE != T16_PREFILL || NW == 4 || 16 * NW == prefill_tile_rows(D), "host and kernel tile rows differ");
   static_assert(prefill_block_keys() % KB == 0, "host blocks are whole kernel blocks");
   static_assert(DL >= 1 && ROWB <= 1024, "a DMA instruction covers whole key rows");
   __shared__ __attribute__((aligned(1024))) char smem[DNS * DSTAGE];
@@ -99,6 +99,15 @@ void prefill16_kernel(const AttnParams p) {
     g = rest % p.num_kv_heads;
     qt = rest / p.num_kv_heads;
     b = 0;
+  } else if constexpr (NW == 4) {
+    // 64-row tiles of a short prefill: consecutive tiles go to different
+    // XCDs (the chip's CUs rather than one XCD's L2), heaviest first
+    const int nqt = p.num_qtiles;
+    const int id = blockIdx.x;
+    qt = nqt - 1 - id % nqt;
+    const int rest = id / nqt;
+    g = rest % p.num_kv_heads;
+    b = rest / p.num_kv_heads;
   } else {
     // consecutive logical tiles share an XCD; the heaviest tile of a
     // sequence first
@@ -426,6 +435,16 @@ hipError_t launch_prefill16(const AttnParams& p, hipStream_t st) {
     hipLaunchKernelGGL((prefill16_kernel<256, 8, true, T16_PREFILL>), dim3((unsigned)total), dim3(512), 0, st, p);
   else
     hipLaunchKernelGGL((prefill16_kernel<256, 8, false, T16_PREFILL>), dim3((unsigned)total), dim3(512), 0, st, p);
+  return hipGetLastError();
+}
+
+// A short prefill (few 256-row tiles for the chip) over 64-row tiles,
+// 128-dim heads; p.tok_per_tile and p.num_qtiles describe 64-row tiles.
+hipError_t launch_prefill16_small(const AttnParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs));
+  if (p.head_dim != 128) return hipErrorInvalidValue;
+  if (p.window > 0) hipLaunchKernelGGL((prefill16_kernel<128, 4, true, T16_PREFILL>), grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((prefill16_kernel<128, 4, false, T16_PREFILL>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -54,6 +54,15 @@ int main() {
         cpl.prefix_split_keys == 512);
   CHECK(cpl.suffix_splits == 1 && cpl.suffix_pages_per_split == 8);
   CHECK(cpl.workspace_bytes == (size_t)9 * 64 * 32 * 130 * 4);
+  // short prefills (their N*G rows fill fewer 256-row tiles than half the CUs) take 64-row tiles
+  pa_dims mx = dims(32, 547, 512, 32, 8, 128, 64, 4096, 128);
+  CHECK(pa::prefill_small_tiles(&mx, 256));                                   // 9 x 8 = 72 tiles < 128
+  pa_dims pf = dims(4, 32768, 8192, 32, 8, 128, 64, 4096, 128);
+  CHECK(!pa::prefill_small_tiles(&pf, 256));
+  pa_dims m256 = dims(32, 547, 512, 16, 4, 256, 64, 4096, 128);
+  CHECK(!pa::prefill_small_tiles(&m256, 256));                                // 128-dim heads only
+  pa_dims p2k = dims(1, 2048, 2048, 32, 8, 128, 64, 64, 64);
+  CHECK(!pa::prefill_small_tiles(&p2k, 256));                                 // 32 x 8 = 256 tiles
   // 64-dim heads keep the 256-row prefill tiles, about half the CUs busy
   pa_dims c64 = dims(64, 64, 1, 32, 8, 64, 64, 362, 72);
   pa::CascadePlan cp64 = pa::make_cascade_plan(&c64, PA_BF16, 256, 4096, 0);
