@@ -131,6 +131,10 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
       int64_t want = (2 * (int64_t)(cu_count > 0 ? cu_count : 1) + units - 1) / units;
       const int min_pages = (256 + d->page_size - 1) / d->page_size;
       const int64_t cap_pages = (W + min_pages - 1) / min_pages;
+      // Beside prefill or 16-row decode tiles the verification steps are
+      // likely few, and their key loops run while the other launches hold
+      // the chip: at least 8 splits keep those loops short.
+      if ((pl.prefill || pl.dec_small) && want < 8) want = 8;
       if (want > 64) want = 64;
       if (want > cap_pages) want = cap_pages;
       if (want < 1) want = 1;

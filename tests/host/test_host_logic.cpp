@@ -87,11 +87,12 @@ int main() {
   pa::Plan p4 = pa::make_plan(&c4, PA_BF16, 256);
   CHECK(p4.prefill && p4.tok_per_tile == 64 && p4.num_qtiles == 8 && p4.dec_small && p4.dec_big && p4.big_nt == 4);
   CHECK(p4.dec_max_n == 16 && p4.comb_max_n == 16);
-  // the verify-tile launch aims at two workgroups per CU over the 32 x 8
-  // (sequence, KV head) pairs: 2 splits of 64 pages; partials only for the 16
-  // decode-class token slots
-  CHECK(p4.splits == 2 && p4.splits_big == 2 && p4.pages_per_split_big == 64 && p4.ws_tok == 16);
-  CHECK(p4.workspace_bytes == (size_t)2 * 32 * 16 * 32 * 130 * 4);
+  // the verify-tile launch would aim at two workgroups per CU over the 32 x 8
+  // (sequence, KV head) pairs (2 splits), but beside the prefill and 16-row
+  // decode tiles it takes at least 8 (16 pages each); partials only for the
+  // 16 decode-class token slots
+  CHECK(p4.splits == 2 && p4.splits_big == 8 && p4.pages_per_split_big == 16 && p4.ws_tok == 16);
+  CHECK(p4.workspace_bytes == (size_t)8 * 32 * 16 * 32 * 130 * 4);
   // one sequence's 16-token verify block over 2048 positions: 8 splits of
   // 256 keys (the fewest keys a verify split takes)
   pa_dims v1 = dims(1, 16, 16, 32, 8, 128, 64, 32, 32);
