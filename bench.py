@@ -48,7 +48,7 @@ TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.js
                  "prefill_d256": (os.path.join(ROOT, "profiles", "prefill_c6_traffic.json"), "prefill16.hip")}
 # kernel (name prefix, with its head-dim template argument) each traffic file is about
 TRAFFIC_KERNELS = {"decode": "pa::decode_splitkv_kernel<128, 1,", "prefill": "pa::prefill_kernel<128,",
-                   "prefill_d256": "pa::prefill16_kernel<false, false>"}
+                   "prefill_d256": "pa::prefill16_kernel<256, 8, false, 0>"}
 
 
 # ----------------------------------------------------------------------------- accounting
