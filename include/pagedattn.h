@@ -317,8 +317,12 @@ size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn
  * workgroups for two per CU of the current device (three when every sequence
  * has one token, max_query_len == 1, and two are not reached), with at least
  * 128 keys per split and at most 64 splits (page "32. Production attention
- * kernels", How many splits?).  Verification blocks (16 < n*G <= 64 rows) use 8 splits
- * unless dims->num_splits is set.  Returns 1 for invalid dims.
+ * kernels", How many splits?).  Verification blocks (16 < n*G <= 64 rows)
+ * take a count of their own: about two workgroups per CU over the batch's
+ * (sequence, KV head) pairs, at least 8 when prefill or decode-row tiles
+ * share the batch (the few verification steps of a mixed batch then run
+ * short key loops), with at least 256 keys per split and at most 64;
+ * dims->num_splits, when > 0, sets both counts.  Returns 1 for invalid dims.
  */
 int32_t pa_choose_splits(const pa_dims* dims);
 
