@@ -744,6 +744,12 @@ def counter_summary(csv_paths, kernel, drop):
             if k in avg:
                 parts.append(f"{label} per MFMA: {avg[k] / m:.2f}")
         lines.append("; ".join(parts))
+    if "SQ_WAVE_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+        # SQ_WAVE_CYCLES counts resident-wave time in quad-cycles on this chip
+        occ = 4 * avg["SQ_WAVE_CYCLES"] / 1024 / (avg["GRBM_GUI_ACTIVE"] / 8)
+        lines.append(f"achieved occupancy: 4 x SQ_WAVE_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8) = {occ:.2f} waves per SIMD")
+    if "SQ_WAVE_CYCLES" in avg and "SQ_WAIT_ANY" in avg:
+        lines.append(f"SQ_WAIT_ANY / SQ_WAVE_CYCLES: {avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}")
     if "SQ_WAVE_CYCLES" in avg and "SQ_WAIT_INST_LDS" in avg:
         lines.append(f"SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES: {avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f}")
     if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
