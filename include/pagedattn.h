@@ -87,7 +87,9 @@ typedef struct pa_dims {
   int64_t o_stride_head;
   int64_t kv_stride_page;  /* pools: element strides of page, slot and head;       */
   int64_t kv_stride_slot;  /* the default layout [P, ps, Hkv, D] has               */
-  int64_t kv_stride_head;  /* (ps*Hkv*D, Hkv*D, D).  K and V share the strides.    */
+  int64_t kv_stride_head;  /* (ps*Hkv*D, Hkv*D, D).  K and V share the strides;   */
+                           /* kv_stride_slot < 2^26 (16 slots of a tile stay      */
+                           /* within 32-bit byte offsets), else UNSUPPORTED.      */
 } pa_dims;
 
 /*

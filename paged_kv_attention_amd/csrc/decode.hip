@@ -120,7 +120,9 @@ void decode_splitkv_kernel(const AttnParams p) {
   const int split = hf ? blockIdx.z : blockIdx.x;
   const int g = hf ? blockIdx.x : blockIdx.y;
   const int b = hf ? blockIdx.y : blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is wave-uniform: chunk positions, page lookups and tile
+  // addresses derived from it stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
@@ -237,59 +239,94 @@ void decode_splitkv_kernel(const AttnParams p) {
   const char* kbase = (const char*)p.k_pool + (int64_t)g * p.kv_stride_head * C::EB;
   const char* vbase = (const char*)p.v_pool + (int64_t)g * p.kv_stride_head * C::EB;
 
-  // Address of slot `sl` of the page holding 16-key tile starting at key `kt`
-  // (tiles never straddle pages: ps is a multiple of 16).  A tile past the
-  // sequence's last page re-reads that page; its keys are masked.
-  auto tile_off = [&](int kt, int sl) -> int64_t {
-    int lp = kt / ps;
-    const int slot = kt - lp * ps + sl;
+  // A 16-key tile never straddles a page (ps is a multiple of 16): its
+  // address is a wave-uniform base (page, first slot) plus a per-lane offset
+  // that is the same for every chunk.  A tile past the sequence's last page
+  // re-reads that page; its keys are masked.
+  const int pshift = __builtin_ctz(ps);          // ps is a power of two
+  const int64_t se = p.kv_stride_slot * C::EB;   // bytes per slot
+  constexpr int KPL = 64 / C::CPL;               // keys per V load of the wave
+  // K: key l16 of the tile, 16-byte piece q4 of each 64-byte step; V load i:
+  // key i * KPL + lane / CPL of the chunk, 16-byte piece lane % CPL.  The host
+  // keeps 16 slots of a tile below 2^31 bytes.
+  const uint32_t koff = (uint32_t)(l16 * se) + 16 * q4;
+  const uint32_t voff = (uint32_t)((lane / C::CPL) * se) + 16 * (lane % C::CPL);
+  struct TileAt {
+    int page, slot;                              // page id and first slot of the tile
+  };
+  auto tile_at = [&](int kt) -> TileAt {
+    int lp = kt >> pshift;
+    const int sl = kt - (lp << pshift);
     lp = min(lp, npages - 1);
-    const int pg = page_of(p, b, lp);
-    return (int64_t)pg * p.kv_stride_page + (int64_t)slot * p.kv_stride_slot;
+    return TileAt{page_of(p, b, lp), sl};
   };
 
   auto load = [&](int c, DecodeChunk<D, KQ>& ch) {
     const int k0 = k_begin + c * C::KC;
+    if constexpr (QUANT) {
+      // 1-byte codes take the per-lane form of the same addresses: uniform
+      // bases for two chunks in flight, beside the scale pointers and
+      // strides, need more scalar registers than the kernel has left
+      auto tile_off = [&](int kt, int sl) -> int64_t {
+        int lp = kt >> pshift;
+        const int slot = kt - (lp << pshift) + sl;
+        lp = min(lp, npages - 1);
+        return (int64_t)page_of(p, b, lp) * p.kv_stride_page + (int64_t)slot * p.kv_stride_slot;
+      };
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if constexpr (QUANT) {
+      for (int t = 0; t < 2; ++t) {
         const char* kp = kbase + tile_off(k0 + 16 * t, l16) + 16 * q4;
 #pragma unroll
         for (int j = 0; j < C::DS / 2; ++j) ch.k[t][j] = *(const u32x4*)(kp + 64 * j);
-      } else {
-        const char* kp = kbase + (tile_off(k0 + 16 * t, l16) + 8 * q4) * C::EB;
-#pragma unroll
-        for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const bf16x8*)(kp + 32 * s * C::EB);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int idx = i * 64 + lane;
-      const int kl = idx / C::CPL, cc = idx % C::CPL;
-      const int t = (i * 64 / C::CPL) / 16;       // uniform per load
-      const char* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) * C::EB + 16 * cc;
-      // a wave's V load covers whole rows (full cache lines) that no other
-      // workgroup reads: a streaming (nontemporal) load reads them faster.
-      // In a 32- or 64-row tile the waves of the other row groups read the
-      // same rows, from the cache.
-      if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
-      else ch.v[i] = *(const u32x4*)vp;
-    }
-    if constexpr (QUANT) {
+      for (int i = 0; i < C::VLOADS; ++i) {
+        const int idx = i * 64 + lane;
+        const int kl = idx / C::CPL, cc = idx % C::CPL;
+        const int t = (i * KPL) / 16;             // uniform per load
+        const char* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) + 16 * cc;
+        if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
+        else ch.v[i] = *(const u32x4*)vp;
+      }
       // lane l: scale of key k0 + l % 32, of K for l < 32 and of V above;
       // keys outside the split (or below every window) get 0, so a stale
       // scale in an unused slot never meets a probability
       const int kk = k0 + (lane & 31);
-      const int lp = kk / ps;                    // a key past the last page reads that page's
+      const int lp = kk >> pshift;               // a key past the last page reads that page's
       const int64_t so = (int64_t)page_of(p, b, min(lp, npages - 1)) * p.sc_stride_page +   // slot kk % ps
-                         (int64_t)(kk - lp * ps) * p.sc_stride_slot + (int64_t)g * p.sc_stride_head;
+                         (int64_t)(kk - (lp << pshift)) * p.sc_stride_slot + (int64_t)g * p.sc_stride_head;
       const float sv = (lane < 32 ? p.k_scale : p.v_scale)[so];
       ch.sc = (kk < k_end && (!WIN || kk >= wlo)) ? sv : 0.f;
+    } else {
+      int64_t tb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const TileAt ta = tile_at(k0 + 16 * t);
+        tb[t] = (int64_t)ta.page * p.kv_stride_page * C::EB + ta.slot * se;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const char* kp = kbase + tb[t] + koff;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const bf16x8*)(kp + 32 * s * C::EB);
+      }
+#pragma unroll
+      for (int i = 0; i < C::VLOADS; ++i) {
+        const int t = (i * KPL) / 16;             // uniform per load
+        const char* vp = vbase + tb[t] + (i * KPL - 16 * t) * se + voff;
+        // a wave's V load covers whole rows (full cache lines) that no other
+        // workgroup reads: a streaming (nontemporal) load reads them faster.
+        // In a 32- or 64-row tile the waves of the other row groups read the
+        // same rows, from the cache.
+        if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
+        else ch.v[i] = *(const u32x4*)vp;
+      }
     }
   };
 
   auto process = [&](int c, const DecodeChunk<D, KQ>& ch) {
     const int k0 = k_begin + c * C::KC;
+    // the chunk reaches the causal diagonal, the split's end or a window edge
     const bool need_mask = k0 + C::KC > mask_lim || k0 < win_all;
     // V chunk -> this wave's LDS tile as bf16; rows past the split's end or
     // before every row's window are selected to zero
@@ -370,8 +407,8 @@ void decode_splitkv_kernel(const AttnParams p) {
         }
       float cmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                          fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+      cmax = xor16_max(cmax);
+      cmax = xor32_max(cmax);
       const float m_new = fmaxf(m_run[nt], cmax);
       const float m_safe = m_new == kNegInf ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[nt] - m_safe);

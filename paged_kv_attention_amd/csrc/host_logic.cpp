@@ -38,6 +38,8 @@ pa_status check_dims(const pa_dims* d, pa_dtype dtype) {
   const int64_t vec = dtype == PA_BF16 ? 8 : 4;
   for (int64_t x : s)
     if (x % vec) return PA_ERR_UNSUPPORTED;
+  // the kernels address the 16 slots of a key tile with 32-bit byte offsets
+  if (d->kv_stride_slot >= ((int64_t)1 << 26)) return PA_ERR_UNSUPPORTED;
   const int G = d->num_q_heads / d->num_kv_heads;
   if (dtype == PA_BF16 && G > 64) return PA_ERR_UNSUPPORTED;
   // grid limits (y and z dimensions are 16-bit)

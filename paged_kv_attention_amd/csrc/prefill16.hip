@@ -48,18 +48,6 @@
 
 namespace pa {
 
-// Reductions across lanes i and i ^ 16 on the gfx950 row-pair swap (no LDS
-// round trip); the swap returns, in some order, the lane's own value and
-// its partner's.
-__device__ __forceinline__ float xor16_max(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // s_waitcnt immediate (gfx9 layout): at most n vector-memory operations in
 // flight, the other counters not waited on
 constexpr int vm_wait16(int n) { return 0x3f70 | (n & 0xf) | ((n >> 4) << 14); }

@@ -152,6 +152,11 @@ int main() {
   CHECK(pa::check_dims(&bad, PA_F32) == PA_OK);     // 4-element multiple suffices for float32
   bad = c3; bad.q_stride_head = 64;
   CHECK(pa::check_dims(&bad, PA_BF16) == PA_ERR_SHAPE);
+  bad = c3; bad.kv_stride_slot = (int64_t)1 << 26;   // tile offsets past 32 bits
+  bad.kv_stride_page = bad.kv_stride_slot * bad.page_size;
+  CHECK(pa::check_dims(&bad, PA_BF16) == PA_ERR_UNSUPPORTED);
+  bad.kv_stride_slot = ((int64_t)1 << 26) - 8;
+  CHECK(pa::check_dims(&bad, PA_BF16) == PA_OK);
   CHECK(pa::check_dims(nullptr, PA_BF16) == PA_ERR_NULL);
 
   // validate_host
