@@ -101,7 +101,7 @@ struct DecodeChunk {
 // loop).  FW: the launch also writes the step's new rows (bf16 pools, 16-row
 // tiles; see the main loop).
 template <int D, int NT, bool WIN, int KQ, int NB = 0, bool FW = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 && (WIN || KQ != KV_BF16) ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 && (WIN || KQ != KV_BF16 || NT == 2) ? 1 : 2)))
 void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D, KQ>;
   constexpr bool QUANT = KQ != KV_BF16;
@@ -261,70 +261,55 @@ void decode_splitkv_kernel(const AttnParams p) {
     return TileAt{page_of(p, b, lp), sl};
   };
 
-  auto load = [&](int c, DecodeChunk<D, KQ>& ch) {
+  auto load = [&](int c, DecodeChunk<D, KQ>& ch) __attribute__((always_inline)) {
     const int k0 = k_begin + c * C::KC;
-    if constexpr (QUANT) {
-      // 1-byte codes take the per-lane form of the same addresses: uniform
-      // bases for two chunks in flight, beside the scale pointers and
-      // strides, need more scalar registers than the kernel has left
-      auto tile_off = [&](int kt, int sl) -> int64_t {
-        int lp = kt >> pshift;
-        const int slot = kt - (lp << pshift) + sl;
-        lp = min(lp, npages - 1);
-        return (int64_t)page_of(p, b, lp) * p.kv_stride_page + (int64_t)slot * p.kv_stride_slot;
-      };
+    TileAt ta[2];
+    int64_t tb[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const char* kp = kbase + tile_off(k0 + 16 * t, l16) + 16 * q4;
+    for (int t = 0; t < 2; ++t) {
+      ta[t] = tile_at(k0 + 16 * t);
+      tb[t] = (int64_t)ta[t].page * p.kv_stride_page * C::EB + ta[t].slot * se;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const char* kp = kbase + tb[t] + koff;
+      if constexpr (QUANT) {
 #pragma unroll
         for (int j = 0; j < C::DS / 2; ++j) ch.k[t][j] = *(const u32x4*)(kp + 64 * j);
-      }
-#pragma unroll
-      for (int i = 0; i < C::VLOADS; ++i) {
-        const int idx = i * 64 + lane;
-        const int kl = idx / C::CPL, cc = idx % C::CPL;
-        const int t = (i * KPL) / 16;             // uniform per load
-        const char* vp = vbase + tile_off(k0 + 16 * t, kl - 16 * t) + 16 * cc;
-        if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
-        else ch.v[i] = *(const u32x4*)vp;
-      }
-      // lane l: scale of key k0 + l % 32, of K for l < 32 and of V above;
-      // keys outside the split (or below every window) get 0, so a stale
-      // scale in an unused slot never meets a probability
-      const int kk = k0 + (lane & 31);
-      const int lp = kk >> pshift;               // a key past the last page reads that page's
-      const int64_t so = (int64_t)page_of(p, b, min(lp, npages - 1)) * p.sc_stride_page +   // slot kk % ps
-                         (int64_t)(kk - (lp << pshift)) * p.sc_stride_slot + (int64_t)g * p.sc_stride_head;
-      const float sv = (lane < 32 ? p.k_scale : p.v_scale)[so];
-      ch.sc = (kk < k_end && (!WIN || kk >= wlo)) ? sv : 0.f;
-    } else {
-      int64_t tb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const TileAt ta = tile_at(k0 + 16 * t);
-        tb[t] = (int64_t)ta.page * p.kv_stride_page * C::EB + ta.slot * se;
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const char* kp = kbase + tb[t] + koff;
+      } else {
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) ch.k[t][s] = *(const bf16x8*)(kp + 32 * s * C::EB);
       }
+    }
 #pragma unroll
-      for (int i = 0; i < C::VLOADS; ++i) {
-        const int t = (i * KPL) / 16;             // uniform per load
-        const char* vp = vbase + tb[t] + (i * KPL - 16 * t) * se + voff;
-        // a wave's V load covers whole rows (full cache lines) that no other
-        // workgroup reads: a streaming (nontemporal) load reads them faster.
-        // In a 32- or 64-row tile the waves of the other row groups read the
-        // same rows, from the cache.
-        if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
-        else ch.v[i] = *(const u32x4*)vp;
-      }
+    for (int i = 0; i < C::VLOADS; ++i) {
+      const int t = (i * KPL) / 16;               // uniform per load
+      const char* vp = vbase + tb[t] + (i * KPL - 16 * t) * se + voff;
+      // a wave's V load covers whole rows (full cache lines) that no other
+      // workgroup reads: a streaming (nontemporal) load reads them faster.
+      // In a 32- or 64-row tile the waves of the other row groups read the
+      // same rows, from the cache.
+      if constexpr (NT == 1) ch.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
+      else ch.v[i] = *(const u32x4*)vp;
+    }
+    if constexpr (QUANT) {
+      // lane l: scale of key k0 + l % 32, of K for l < 32 and of V above, in
+      // K's tile (l & 16) / 16 (keys outside the split are zeroed where the
+      // chunk is used, so this load is not waited for here)
+      const bool hi = (lane & 16) != 0;
+      const int spage = hi ? ta[1].page : ta[0].page, sslot = (hi ? ta[1].slot : ta[0].slot) + (lane & 15);
+      const int64_t so = (int64_t)spage * p.sc_stride_page + (int64_t)sslot * p.sc_stride_slot +
+                         (int64_t)g * p.sc_stride_head;
+      // one base and a uniform byte distance, not a choice between two
+      // pointers of the argument block (which would move the whole block to
+      // scratch memory)
+      const char* ksb = (const char*)p.k_scale;
+      const int64_t vdist = (const char*)p.v_scale - ksb;
+      ch.sc = *(const float*)(ksb + (lane < 32 ? 0 : vdist) + so * 4);
     }
   };
 
-  auto process = [&](int c, const DecodeChunk<D, KQ>& ch) {
+  auto process = [&](int c, const DecodeChunk<D, KQ>& ch) __attribute__((always_inline)) {
     const int k0 = k_begin + c * C::KC;
     // the chunk reaches the causal diagonal, the split's end or a window edge
     const bool need_mask = k0 + C::KC > mask_lim || k0 < win_all;
@@ -354,7 +339,14 @@ void decode_splitkv_kernel(const AttnParams p) {
     }
     f32x4 ksc[2], vsc[2];                         // quantized: scales of keys 16t + 4*q4 + r
     if constexpr (QUANT) {
-      scl[lane] = ch.sc;
+      // keys outside the split (or below every window) get scale 0, so a
+      // stale scale in an unused slot never meets a probability
+      float sc = ch.sc;
+      if (need_mask) {
+        const int kk = k0 + (lane & 31);
+        if (!(kk < k_end && (!WIN || kk >= wlo))) sc = 0.f;
+      }
+      scl[lane] = sc;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         ksc[t] = *(const PA_LDS f32x4*)(scl + 16 * t + 4 * q4);
@@ -502,17 +494,37 @@ void decode_splitkv_kernel(const AttnParams p) {
   // a row group past the step's rows has nothing to compute (its waves
   // still take part in the merge)
   const int my_chunks = 16 * rg < rows ? nchunks : 0;
-#pragma unroll
-  for (int j = 0; j < NBUF - 1; ++j)
-    if (kg + KG * j < my_chunks) load(kg + KG * j, buf[j]);
-  for (int base = kg; base < my_chunks; base += KG * NBUF) {
-#pragma unroll
-    for (int k = 0; k < NBUF; ++k) {
-      const int c = base + KG * k;
-      const int cn = c + KG * (NBUF - 1);
-      if (cn < my_chunks) load(cn, buf[(k + NBUF - 1) % NBUF]);
-      if (c < my_chunks) process(c, buf[k]);
+  // this wave's chunks kg, kg + KG, ...: n_w of them, chunk i in buffer i % NBUF
+  const int n_w = my_chunks > kg ? (my_chunks - kg + KG - 1) / KG : 0;
+  auto chunk = [&](int i) { return kg + KG * i; };
+  if constexpr (NBUF == 1) {
+    for (int i = 0; i < n_w; ++i) {
+      load(chunk(i), buf[0]);
+      process(chunk(i), buf[0]);
     }
+  } else {
+    static_assert(NBUF == 2, "register chunks per wave: 1 or 2");
+    int i0 = 0;
+    if (n_w >= 3) {
+      // Steady state with every load unconditional: the compiler's memory
+      // counters then know which loads each buffer waits for.  (After a
+      // load that may be skipped they must assume the fewest loads in
+      // flight, and processing a chunk would wait for the chunk requested
+      // after it too.)
+      load(chunk(0), buf[0]);
+      for (; i0 + 3 <= n_w; i0 += 2) {
+        load(chunk(i0 + 1), buf[1]);
+        process(chunk(i0), buf[0]);
+        load(chunk(i0 + 2), buf[0]);
+        process(chunk(i0 + 1), buf[1]);
+      }
+    } else if (n_w > 0) {
+      load(chunk(0), buf[0]);
+    }
+    // fewer than three chunks left; chunk i0 is in flight
+    if (i0 + 1 < n_w) load(chunk(i0 + 1), buf[1]);
+    if (i0 < n_w) process(chunk(i0), buf[0]);
+    if (i0 + 1 < n_w) process(chunk(i0 + 1), buf[1]);
   }
 
   // ---- merge the states of the waves of each row group (fixed order:
