@@ -454,15 +454,11 @@ void decode_splitkv_kernel(const AttnParams p) {
     }
   };
 
-  // Register pipeline of NBUF chunks per wave: chunk c + KG*(NBUF-1) is
-  // loaded while chunk c is computed.  NBUF = 1 (load a chunk, then compute it) is
-  // the measured best on the 64 x 4096 decode step: a second chunk in flight
-  // per wave (register double buffering, or issuing the next chunk's loads
-  // before this chunk's softmax) lowers the achieved HBM bandwidth.  A launch
-  // with fewer workgroups than that (more than one split: the batch has too
-  // few (sequence, KV head) pairs to fill the chip, and its longest splits
-  // finish alone) keeps two chunks per wave in flight instead (NB = 2, for
-  // heads of up to 128 dims).
+  // Register pipeline of NBUF chunks per wave: chunk i + 1 of the wave is
+  // loaded while chunk i is computed (NBUF = 2; the launch picks it for
+  // heads of up to 128 dims and for quantized pools), or each chunk is
+  // loaded, then computed (NBUF = 1).  On the 64 x 4096 decode step two
+  // chunks in flight measured 1 % faster than one.
   constexpr int NBUF = NB ? NB : C::NBUF;
   DecodeChunk<D, KQ> buf[NBUF];
 
@@ -703,31 +699,28 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
       else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_FP8>), grid, dim3(256), 0, st, p);
       break;
     default:
-      // two chunks per wave in flight for split launches (see the main loop);
-      // 256-dim heads do not have the registers for it
+      // Two chunks per wave in flight (see the main loop) for heads of up to
+      // 128 dims: always in 16-row tiles, in 32- and 64-row tiles when the
+      // launch has several splits; 256-dim heads do not have the registers
       if constexpr (NT == 1) {
         if (p.new_k) {                           // the step's new rows written by this launch
-          if constexpr (D <= 128) {
-            if (p.num_splits > 1) {
-              if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2, true>), grid, dim3(256), 0, st, p);
-              else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 2, true>), grid, dim3(256), 0, st, p);
-              break;
-            }
-          }
-          if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 0, true>), grid, dim3(256), 0, st, p);
-          else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 0, true>), grid, dim3(256), 0, st, p);
+          constexpr int NBW = D <= 128 ? 2 : 0;
+          if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, NBW, true>), grid, dim3(256), 0, st, p);
+          else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, NBW, true>), grid, dim3(256), 0, st, p);
           break;
         }
       }
       if constexpr (D <= 128) {
-        if (p.num_splits > 1) {
+        if (NT == 1 || p.num_splits > 1) {
           if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2>), grid, dim3(256), 0, st, p);
           else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 2>), grid, dim3(256), 0, st, p);
           break;
         }
       }
-      if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16>), grid, dim3(256), 0, st, p);
+      if constexpr (NT > 1 || D > 128) {
+        if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16>), grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16>), grid, dim3(256), 0, st, p);
+      }
   }
   return hipGetLastError();
 }
