@@ -267,10 +267,9 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
   p.context_lens = context_lens;
   p.query_start_loc = query_start_loc;
   const int N = dims->num_tokens, Hq = dims->num_q_heads;
-  const int smax = pl.splits > pl.splits_big ? pl.splits : pl.splits_big;
-  if (smax > 1) {
+  if (pl.ws_splits > 1) {
     p.ws_acc = (float*)workspace;
-    p.ws_ml = (float*)workspace + (size_t)smax * dims->num_seqs * pl.ws_tok * Hq * dims->head_dim;
+    p.ws_ml = (float*)workspace + (size_t)pl.ws_splits * dims->num_seqs * pl.ws_tok * Hq * dims->head_dim;
   }
   p.q_stride_tok = dims->q_stride_tok;
   p.q_stride_head = dims->q_stride_head;
@@ -365,6 +364,16 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
     if (e == hipSuccess) e = launch_f32(p, s);
     if (e == hipSuccess && pl.combine) e = launch_combine(p, false, s);
   } else {
+    if (pl.bal_wgs > 0) {
+      // balanced 16-row tiles: partial slots b + w (w: the wave), then the
+      // combine's map
+      const size_t rows = (size_t)(dims->num_seqs + 4 * pl.bal_wgs) * pl.ws_tok * Hq;
+      p.bal_wgs = pl.bal_wgs;
+      p.bal_min_chunks = pl.bal_min_chunks;
+      p.bal_acc = (float*)((char*)workspace + pl.bal_offset);
+      p.bal_ml = p.bal_acc + rows * dims->head_dim;
+      p.bal_meta = (int32_t*)(p.bal_ml + rows * 2);
+    }
     AttnParams q1 = p;                       // 16-row decode tiles
     q1.row_lo = 0;
     q1.row_hi = 16;
@@ -385,10 +394,11 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
       }
       return launch_prefill(p, st);
     };
-    // New rows: a batch of 16-row decode tiles alone writes them inside its
-    // decode launch (each workgroup the rows of its own KV head and pages,
-    // before it reads a key); otherwise they are written first.
-    const bool fuse = wp.num_tokens > 0 && classes == 1 && pl.dec_small;
+    // New rows: a batch of 16-row decode tiles alone on a split launch writes
+    // them inside its decode launch (each workgroup the rows of its own KV
+    // head and pages, before it reads a key); otherwise they are written
+    // first.
+    const bool fuse = wp.num_tokens > 0 && classes == 1 && pl.dec_small && pl.bal_wgs == 0;
     if (wp.num_tokens > 0 && !fuse && launch_kv_write(wp, s) != hipSuccess) return PA_ERR_LAUNCH;
     // The side streams are made on the first bf16 call of any kind: HIP deals
     // streams to the process's few hardware queues in the order they are

@@ -297,20 +297,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
   const int tok = s0 + t;
   // rows of the 16-row decode tile and of the verify tile may use different
   // split counts; a class with one split was written by its decode kernel
-  const int S = n * p.group <= 16 ? p.comb_splits_small : p.comb_splits_big;
-  if (S <= 1) return;
+  int S = n * p.group <= 16 ? p.comb_splits_small : p.comb_splits_big;
   const float* acc_p = p.ws_acc;
   const float* ml_p = p.ws_ml;
   // workspace rows per split: (sequence, step token) slots, or flat tokens
-  const int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
-  const int64_t row = p.ws_flat ? (int64_t)tok * p.num_q_heads + h : ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
+  int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
+  int64_t row = p.ws_flat ? (int64_t)tok * p.num_q_heads + h : ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
+  int s_base = 0;
+  if (p.bal_wgs > 0 && n * p.group <= 16) {
+    // balanced 16-row tiles: the sequence's pieces hold slots s_base ..
+    // s_base + S - 1 of ws_tok * Hq rows each (one piece: written by the
+    // decode kernel)
+    s_base = p.bal_meta[2 * b];
+    S = p.bal_meta[2 * b + 1];
+    acc_p = p.bal_acc;
+    ml_p = p.bal_ml;
+    NH = (int64_t)p.ws_tok * p.num_q_heads;
+    row = (int64_t)t * p.num_q_heads + h;
+  }
+  if (S <= 1) return;
   // this group's maximum, four splits' loads in flight at a time; padding
   // entries are (-inf, 0) and leave every sum bit for bit unchanged
   float M = kNegInf;
   for (int s = grp; s < S; s += 4 * NGR) {
     float m[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = s + j * NGR < S ? ml_p[((s + j * NGR) * NH + row) * 2] : kNegInf;
+    for (int j = 0; j < 4; ++j) m[j] = s + j * NGR < S ? ml_p[((s_base + s + j * NGR) * NH + row) * 2] : kNegInf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) M = fmaxf(M, m[j]);
   }
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     for (int j = 0; j < 4; ++j) {
       const int sj = s + j * NGR;
       if (sj < S) {
-        const int64_t ri = sj * NH + row;
+        const int64_t ri = (s_base + sj) * NH + row;
         ml[j] = *(const f32x2*)(ml_p + ri * 2);
         av[j] = *(const f32x4*)(acc_p + ri * D + 4 * c4);
       } else {

@@ -81,7 +81,11 @@ struct DecodeLds {
   static constexpr int ORS = D + 4;              // merge buffer row stride in floats
   static constexpr int STAGE = 4 * DecodeCfg<D, KQ>::WAVE_LDS;
   static constexpr int MERGE = (128 + ROWS * ORS) * 4;
-  static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
+  static constexpr int MAIN = STAGE > MERGE ? STAGE : MERGE;
+  // balanced launches (16-row tiles): chunk counts and prefix sums of the
+  // batch's sequences and the four waves' sums, kept across pieces
+  static constexpr int BAL = NT == 1 ? (2 * bal_max_seqs() + 16) * 4 : 0;
+  static constexpr int BYTES = MAIN + BAL;
 };
 
 template <int D, int KQ>
@@ -100,7 +104,7 @@ struct DecodeChunk {
 // NB: register chunks per wave, 0 for the code type's default (see the main
 // loop).  FW: the launch also writes the step's new rows (bf16 pools, 16-row
 // tiles; see the main loop).
-template <int D, int NT, bool WIN, int KQ, int NB = 0, bool FW = false>
+template <int D, int NT, bool WIN, int KQ, int NB = 0, bool FW = false, bool BAL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 && (WIN || KQ != KV_BF16 || NT == 2) ? 1 : 2)))
 void decode_splitkv_kernel(const AttnParams p) {
   using C = DecodeCfg<D, KQ>;
@@ -109,29 +113,155 @@ void decode_splitkv_kernel(const AttnParams p) {
   constexpr int ORS = DecodeLds<D, NT, KQ>::ORS;
   __shared__ __attribute__((aligned(16))) char smem[DecodeLds<D, NT, KQ>::BYTES];
 
-  // Grid order.  The hardware deals workgroups to the 8 XCDs in turn.  With
-  // the split fastest, split 0 (the longest) of every sequence lands on the
-  // same XCDs; a batch of decode tiles alone therefore runs with the KV head
-  // fastest, which gives each XCD the same heads of every sequence and split,
-  // an equal share of the work however ragged the sequences are.  Batches
-  // with prefill or verification tiles beside keep the split fastest, which
-  // measured faster there.
-  const bool hf = NT == 1 && p.head_first;
-  const int split = hf ? blockIdx.z : blockIdx.x;
-  const int g = hf ? blockIdx.x : blockIdx.y;
-  const int b = hf ? blockIdx.y : blockIdx.z;
   // the wave index is wave-uniform: chunk positions, page lookups and tile
   // addresses derived from it stay in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
+  const int G = p.group;
+
+  // The workgroup's work is a list of pieces: sequence b, its keys
+  // [k_begin, k_end).  A split launch has one, split `split` of sequence b.
+  // Grid order: the hardware deals workgroups to the 8 XCDs in turn.  With
+  // the split fastest, split 0 (the longest) of every sequence lands on the
+  // same XCDs; a batch of decode tiles alone therefore runs with the KV head
+  // fastest, which gives each XCD the same heads of every sequence and
+  // split, an equal share of the work however ragged the sequences are.
+  // Batches with prefill or verification tiles beside keep the split
+  // fastest, which measured faster there.
+  // A balanced launch (16-row tiles, grid (KV head, bal_wgs)) lays the
+  // batch's 32-key chunks end to end and gives wave w = 4 u + (wave index)
+  // the R chunks from w R on, one piece per sequence they touch: every wave,
+  // and with two workgroups per CU every CU, reads the same bytes however
+  // ragged the batch is (a CU streams about 30 GB/s, so the CU with the most
+  // bytes would set the time).  Each wave takes its pieces on its own (no
+  // barrier between them) and writes each piece's partial state; a piece
+  // holding all of a sequence is written normalised.
+  constexpr bool bal = BAL;
+  static_assert(!BAL || NT == 1, "balanced launches take 16-row tiles");
+  // a balanced launch's waves take their pieces apart: no workgroup barrier
+  // after the prologue (the step's new rows are written before it)
+  static_assert(!(BAL && FW), "balanced launches do not write the new rows");
+  int g = 0, split = 0, bnext = 0, bend = 0, bal_lo = 0, bal_hi = 0, bal_u = 0;
+  const int* Cs = nullptr;                      // balanced: chunks per sequence (-1: of this launch, no keys)
+  const int* Qs = nullptr;                      // balanced: chunks of the sequences before it
+  if constexpr (BAL) {
+    g = blockIdx.x;
+    bal_u = blockIdx.y;
+    int* cs = (int*)(smem + DecodeLds<D, NT, KQ>::MAIN);
+    int* qs = cs + bal_max_seqs();
+    int* wsum = qs + bal_max_seqs();
+    const int B = p.num_seqs;                   // at most bal_max_seqs() (host rule)
+    const int tid = threadIdx.x;
+    // chunks of sequences 2 tid and 2 tid + 1 (0: another launch's)
+    int cnt[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int bb = 2 * tid + j;
+      int c = 0;
+      if (bb < B) {
+        const int sb = p.query_start_loc[bb], nb = p.query_start_loc[bb + 1] - sb;
+        if (nb > 0 && nb <= p.dec_max_n && nb * G > p.row_lo && nb * G <= p.row_hi && nb <= p.ws_tok) {
+          const int Lb = clampi(p.context_lens[bb], 0, p.table_width * p.page_size);
+          const int wl = WIN ? max(p.window > 0 ? max(0, Lb - nb - p.window + 1) : 0, p.key_lo) : 0;
+          const int kb = wl & ~15;
+          c = Lb > kb ? (Lb - kb + C::KC - 1) / C::KC : -1;
+        }
+      }
+      cnt[j] = c;
+    }
+    // exclusive prefix sums of the chunk counts over the workgroup
+    const int loc = max(cnt[0], 0) + max(cnt[1], 0);
+    int inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int v = wsum[w];
+      before += w < wave ? v : 0;
+      total += v;
+    }
+    const int ex = before + inc - loc;
+    cs[2 * tid] = cnt[0];
+    cs[2 * tid + 1] = cnt[1];
+    qs[2 * tid] = ex;
+    qs[2 * tid + 1] = ex + max(cnt[0], 0);
+    __syncthreads();
+    const int nw = 4 * p.bal_wgs;               // waves per KV head
+    const int R = max(p.bal_min_chunks, (total + nw - 1) / nw);
+    bal_u = 4 * bal_u + wave;                   // from here on: the wave's index
+    bal_lo = min(bal_u * R, total);
+    bal_hi = min(bal_lo + R, total);
+    // for the combine: the first partial slot of each sequence and how many
+    // pieces it has (0 or 1: no partials)
+    if (g == 0 && blockIdx.y == 0)
+      for (int bb = tid; bb < B; bb += 256) {
+        const int c = cs[bb], q = qs[bb];
+        p.bal_meta[2 * bb] = bb + q / R;
+        p.bal_meta[2 * bb + 1] = c > 0 ? (q + c - 1) / R - q / R + 1 : 0;
+      }
+    // rows of a sequence of this launch without any key are zero
+    if (blockIdx.y == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (cnt[j] < 0) {
+          const int bb = 2 * tid + j;
+          const int sb = p.query_start_loc[bb], nb = p.query_start_loc[bb + 1] - sb;
+          for (int r = 0; r < nb * G; ++r) {
+            __bf16* op = (__bf16*)p.out + (int64_t)(sb + r / G) * p.o_stride_tok + (int64_t)(g * G + r % G) * p.o_stride_head;
+            for (int d = 0; d < D; d += 8) *(u32x4*)(op + d) = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+    }
+    // the first sequence whose chunks reach bal_lo: the last one whose
+    // prefix is at most bal_lo (it has chunks: the next prefix is larger)
+    bnext = bend = B;
+    if (bal_lo < bal_hi) {
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qs[mid] <= bal_lo) lo = mid;
+        else hi = mid - 1;
+      }
+      bnext = __builtin_amdgcn_readfirstlane(lo);
+    }
+    Cs = cs;
+    Qs = qs;
+  } else {
+    const bool hf = NT == 1 && p.head_first;
+    split = hf ? blockIdx.z : blockIdx.x;
+    g = hf ? blockIdx.x : blockIdx.y;
+    bnext = hf ? blockIdx.y : blockIdx.z;
+    bend = bnext + 1;
+  }
+  for (; bnext < bend; ++bnext) {
+  const int b = bnext;
+  int c_lo = 0, c_hi = 0;                       // balanced: the piece's chunks of sequence b
+  bool whole;                                   // the piece holds all of the row's keys
+  if (bal) {
+    const int cb = __builtin_amdgcn_readfirstlane(Cs[b]);
+    const int qb = __builtin_amdgcn_readfirstlane(Qs[b]);
+    if (qb >= bal_hi) break;
+    if (cb <= 0) continue;
+    c_lo = max(bal_lo, qb) - qb;
+    c_hi = min(bal_hi, qb + cb) - qb;
+    whole = c_lo == 0 && c_hi == cb;
+  } else {
+    whole = p.num_splits == 1 && !p.force_partial;
+  }
+  const bool first = bal ? c_lo == 0 : split == 0;   // the piece with the row's first keys (sinks)
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
-  const int G = p.group;
   const int rows = n * G;
-  if (n <= 0 || n > p.dec_max_n || rows <= p.row_lo || rows > p.row_hi) return;
+  if (n <= 0 || n > p.dec_max_n || rows <= p.row_lo || rows > p.row_hi) continue;
   // a step longer than the host bound max_query_len (invalid input) would
   // index split partials past its workspace rows: such a sequence is skipped
-  if (!p.ws_flat && n > p.ws_tok && (p.num_splits > 1 || p.force_partial)) return;
+  if (!p.ws_flat && n > p.ws_tok && (bal || p.num_splits > 1 || p.force_partial)) continue;
 
   // Row groups: the step's rows form groups of 16, NG of them in use (the
   // tile's NT, or for a 64-row tile whose step fills at most 32 rows, 2).
@@ -140,8 +270,8 @@ void decode_splitkv_kernel(const AttnParams p) {
   // state of 16 rows only (so a 32- or 64-row tile needs no more registers
   // per wave than the 16-row one, and no wave of a partly filled tile idles).
   const int NG = NT == 4 && rows <= 32 ? 2 : NT;
-  const int KG = 4 / NG;
-  const int rg = wave % NG, kg = wave / NG;
+  const int KG = BAL ? 1 : 4 / NG;               // a balanced wave takes all of its piece's chunks
+  const int rg = BAL ? 0 : wave % NG, kg = BAL ? 0 : wave / NG;
 
   const int ps = p.page_size;
   const int L = clampi(p.context_lens[b], 0, p.table_width * ps);
@@ -154,8 +284,10 @@ void decode_splitkv_kernel(const AttnParams p) {
   const int wlo = WIN ? max(window > 0 ? max(0, L - n - window + 1) : 0, key_lo) : 0;
   const int pg0 = wlo / ps + split * p.pages_per_split;
   const int pg1 = min(pg0 + p.pages_per_split, npages);
-  const int k_begin = WIN ? max(pg0 * ps, wlo & ~15) : pg0 * ps;   // 16-key tiles stay inside pages
-  const int k_end = min(pg1 * ps, L);
+  // 16-key tiles stay inside pages; a balanced piece has chunks [c_lo, c_hi)
+  // of the keys from the 16-key tile of wlo on
+  const int k_begin = bal ? (wlo & ~15) + C::KC * c_lo : WIN ? max(pg0 * ps, wlo & ~15) : pg0 * ps;
+  const int k_end = bal ? min((wlo & ~15) + C::KC * c_hi, L) : min(pg1 * ps, L);
   const int nchunks = k_end > k_begin ? (k_end - k_begin + C::KC - 1) / C::KC : 0;
 
   const int causal = p.causal;
@@ -463,8 +595,8 @@ void decode_splitkv_kernel(const AttnParams p) {
   DecodeChunk<D, KQ> buf[NBUF];
 
   if constexpr (FW) {
-    // The step's new rows of KV head g whose positions fall in this split's
-    // pages go to their slots before any key is read (the write of
+    // The step's new rows of KV head g whose positions fall in this piece's
+    // keys (a split's pages) go to their slots before any key is read (the write of
     // kv_cache_write, done by this launch: no other workgroup reads those
     // positions).  Both rows are loaded before either is stored.  A
     // workgroup barrier orders the stores before every wave's loads: only
@@ -473,9 +605,10 @@ void decode_splitkv_kernel(const AttnParams p) {
     constexpr int CPR = D * 2 / 16;             // 16-byte chunks per row
     for (int c = threadIdx.x; c < n * CPR; c += 256) {
       const int t = c / CPR, cc = c % CPR;
-      const int lp = (L - n + t) / ps;
+      const int pos = L - n + t;
       const int slot = p.new_slots[s0 + t];
-      if (L - n + t >= 0 && lp >= pg0 && lp < pg1 && slot >= 0 && slot < p.num_pages * ps) {
+      if (pos >= 0 && pos >= (bal ? k_begin : pg0 * ps) && pos < (bal ? k_end : pg1 * ps) && slot >= 0 &&
+          slot < p.num_pages * ps) {
         const int64_t src = (int64_t)(s0 + t) * p.new_stride_tok + (int64_t)g * p.new_stride_head + 8 * cc;
         const int64_t dst = (int64_t)(slot / ps) * p.kv_stride_page + (int64_t)(slot % ps) * p.kv_stride_slot +
                             (int64_t)g * p.kv_stride_head + 8 * cc;
@@ -538,6 +671,40 @@ void decode_splitkv_kernel(const AttnParams p) {
       for (int dt = 0; dt < C::DT; ++dt) acc[nt][dt] -= 128.f * s_;
     }
   }
+  if constexpr (BAL) {
+    // the wave's own state of its piece: lane (q4, l16) holds dims
+    // 16 dt + 4 q4 + r of row l16
+    if (l16 < rows) {
+      const int tok = s0 + l16 / G, head = g * G + l16 % G;
+      float M = m_run[0], Lt = l_run[0], e = 1.f;
+      if (p.sinks && first) {
+        // the sink joins the first piece as one more score with no value row
+        const float s2 = p.sinks[head] * kLog2e;
+        const float Mn = fmaxf(M, s2);
+        const float Ms = Mn == kNegInf ? 0.f : Mn;
+        e = fast_exp2(M - Ms);
+        Lt = Lt * e + fast_exp2(s2 - Ms);
+        M = Mn;
+      }
+      if (whole) {
+        const float inv = Lt > 0.f ? e / Lt : 0.f;
+        __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * q4;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const f32x4 o = acc[0][dt];
+          *(u32x2*)(op + 16 * dt) = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+        }
+      } else {
+        // partial slot b + w: unique, since each piece adds one to b or to w
+        const int64_t ri = ((int64_t)(b + bal_u) * p.ws_tok + l16 / G) * p.num_q_heads + head;
+        float* wa = p.bal_acc + ri * D + 4 * q4;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) *(f32x4*)(wa + 16 * dt) = acc[0][dt] * e;
+        if (q4 == 0) *(f32x2*)(p.bal_ml + ri * 2) = f32x2{M, Lt};
+      }
+    }
+    continue;
+  } else {
   __syncthreads();                              // staging tiles are free from here on
   float* Mw = (float*)smem;                     // [4 waves][16 rows of the wave's group]
   float* Lw = Mw + 64;                          // [4 waves][16]
@@ -582,7 +749,7 @@ void decode_splitkv_kernel(const AttnParams p) {
       Lt += Lw[w * 16 + (row & 15)];
     }
     f32x4 o = *(const f32x4*)(Ob + row * ORS + 4 * c4);
-    if (p.sinks && split == 0) {
+    if (p.sinks && first) {
       // the sink joins split 0 as one more score with no value row
       const float s2 = p.sinks[head] * kLog2e;
       const float Mn = fmaxf(M, s2);
@@ -670,7 +837,7 @@ void decode_splitkv_kernel(const AttnParams p) {
       const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
       *(u32x2*)op = u32x2{pack_bf16x2(ot[0] * inv, ot[1] * inv), pack_bf16x2(ot[2] * inv, ot[3] * inv)};
-    } else if (p.num_splits == 1 && !p.force_partial) {
+    } else if (whole) {
       const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
       __bf16* op = (__bf16*)p.out + (int64_t)tok * p.o_stride_tok + (int64_t)head * p.o_stride_head + 4 * c4;
       *(u32x2*)op = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
@@ -682,46 +849,57 @@ void decode_splitkv_kernel(const AttnParams p) {
       if (c4 == 0) *(f32x2*)(p.ws_ml + ri * 2) = f32x2{M, Lt};
     }
   }
+  }
+  }
 }
 
-template <int D, int NT>
-static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
-  const dim3 grid = NT == 1 && p.head_first ? dim3(p.num_kv_heads, p.num_seqs, p.num_splits)
-                                            : dim3(p.num_splits, p.num_kv_heads, p.num_seqs);
+template <int D, int NT, int KQ, int NB, bool FW, bool BAL>
+static void launch_k(const AttnParams& p, bool win, dim3 grid, hipStream_t st) {
+  if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KQ, NB, FW, BAL>), grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KQ, NB, FW, BAL>), grid, dim3(256), 0, st, p);
+}
+
+template <int D, int NT, bool BAL>
+static void launch_decode_b(const AttnParams& p, dim3 grid, hipStream_t st) {
   const bool win = p.window > 0 || p.key_lo > 0;
   switch (p.kv_code) {
     case KV_INT8:
-      if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_INT8>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_INT8>), grid, dim3(256), 0, st, p);
+      launch_k<D, NT, KV_INT8, 0, false, BAL>(p, win, grid, st);
       break;
     case KV_FP8:
-      if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_FP8>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_FP8>), grid, dim3(256), 0, st, p);
+      launch_k<D, NT, KV_FP8, 0, false, BAL>(p, win, grid, st);
       break;
     default:
       // Two chunks per wave in flight (see the main loop) for heads of up to
       // 128 dims: always in 16-row tiles, in 32- and 64-row tiles when the
       // launch has several splits; 256-dim heads do not have the registers
-      if constexpr (NT == 1) {
+      if constexpr (NT == 1 && !BAL) {
         if (p.new_k) {                           // the step's new rows written by this launch
-          constexpr int NBW = D <= 128 ? 2 : 0;
-          if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, NBW, true>), grid, dim3(256), 0, st, p);
-          else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, NBW, true>), grid, dim3(256), 0, st, p);
+          launch_k<D, NT, KV_BF16, D <= 128 ? 2 : 0, true, false>(p, win, grid, st);
           break;
         }
       }
       if constexpr (D <= 128) {
         if (NT == 1 || p.num_splits > 1) {
-          if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16, 2>), grid, dim3(256), 0, st, p);
-          else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16, 2>), grid, dim3(256), 0, st, p);
+          launch_k<D, NT, KV_BF16, 2, false, BAL>(p, win, grid, st);
           break;
         }
       }
-      if constexpr (NT > 1 || D > 128) {
-        if (win) hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, true, KV_BF16>), grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((decode_splitkv_kernel<D, NT, false, KV_BF16>), grid, dim3(256), 0, st, p);
-      }
+      if constexpr (NT > 1 || D > 128) launch_k<D, NT, KV_BF16, 0, false, BAL>(p, win, grid, st);
   }
+}
+
+template <int D, int NT>
+static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
+  if constexpr (NT == 1) {
+    if (p.bal_wgs > 0) {
+      launch_decode_b<D, NT, true>(p, dim3(p.num_kv_heads, p.bal_wgs), st);
+      return hipGetLastError();
+    }
+  }
+  const dim3 grid = NT == 1 && p.head_first ? dim3(p.num_kv_heads, p.num_seqs, p.num_splits)
+                                            : dim3(p.num_splits, p.num_kv_heads, p.num_seqs);
+  launch_decode_b<D, NT, false>(p, grid, st);
   return hipGetLastError();
 }
 

@@ -144,6 +144,24 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
       pl.splits_big = (W + pl.pages_per_split_big - 1) / pl.pages_per_split_big;
     }
     if (!pl.dec_big) pl.splits_big = 1;
+    // Balanced 16-row tiles: where the split launch would cut several
+    // sequences into splits of 2048 keys or more (more than one split: the
+    // batch's (sequence, KV head) pairs cannot fill two workgroups per CU),
+    // a fixed grid of about two workgroups per CU shares the batch's 32-key
+    // chunks equally among its waves instead: the longest splits of a ragged
+    // batch no longer finish alone.  Shorter splits measured as fast as the
+    // balanced launch with its extra partials (a ragged batch of 32 at up to
+    // 4096 positions) or faster (one sequence).  An explicit split count
+    // keeps the split launch.
+    // (the chunk counts stay far inside int)
+    const int64_t max_chunks = (int64_t)d->num_seqs * ((int64_t)W * d->page_size / 32 + 1);
+    if (pl.dec_small && pl.splits > 1 && d->num_splits == 0 && d->num_seqs >= 2 &&
+        d->num_seqs <= bal_max_seqs() && (int64_t)pl.pages_per_split * d->page_size >= 2048 &&
+        max_chunks < ((int64_t)1 << 30)) {
+      const int cu = cu_count > 0 ? cu_count : 1;
+      pl.bal_wgs = (2 * cu + d->num_kv_heads - 1) / d->num_kv_heads;
+      pl.bal_min_chunks = 4;
+    }
     pl.combine = dmax >= 1 && ((pl.dec_small && pl.splits > 1) || (pl.dec_big && pl.splits_big > 1));
     pl.comb_tokens = dmax;
     pl.comb_max_n = pl.dec_max_n;
@@ -158,12 +176,23 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
     pl.comb_max_n = INT_MAX;
     pl.ws_tok = pl.mql;
   }
-  const int smax = pl.splits > pl.splits_big ? pl.splits : pl.splits_big;
+  // split slots of the classes that run split launches
+  pl.ws_splits = pl.bal_wgs > 0 ? pl.splits_big : (pl.splits > pl.splits_big ? pl.splits : pl.splits_big);
   // split partials are indexed by (sequence, token of the step) over the
   // split classes only, so prefill tokens take no workspace
-  if (smax > 1 && pl.combine)
-    pl.workspace_bytes = (size_t)smax * (size_t)d->num_seqs * (size_t)pl.ws_tok * (size_t)d->num_q_heads *
-                         ((size_t)d->head_dim + 2) * 4;
+  size_t bytes = 0;
+  if (pl.ws_splits > 1 && pl.combine)
+    bytes = (size_t)pl.ws_splits * (size_t)d->num_seqs * (size_t)pl.ws_tok * (size_t)d->num_q_heads *
+            ((size_t)d->head_dim + 2) * 4;
+  if (pl.bal_wgs > 0) {
+    // balanced partials: slots b + w < B + 4 bal_wgs (w: the wave) of
+    // ws_tok * Hq rows, then two ints per sequence for the combine
+    bytes = (bytes + 255) & ~(size_t)255;
+    pl.bal_offset = bytes;
+    const size_t rows = (size_t)(d->num_seqs + 4 * pl.bal_wgs) * (size_t)pl.ws_tok * (size_t)d->num_q_heads;
+    bytes += rows * ((size_t)d->head_dim + 2) * 4 + (size_t)d->num_seqs * 8;
+  }
+  pl.workspace_bytes = bytes;
   return pl;
 }
 

@@ -27,6 +27,10 @@ struct Plan {
   int comb_tokens;         // combine: token slots per sequence
   int comb_max_n;          // combine: sequences with n <= comb_max_n
   int ws_tok;              // workspace row slots per sequence
+  int ws_splits;           // split slots of the split launches' partials (1: none)
+  int bal_wgs;             // bf16 16-row tiles: balanced launch, workgroups per KV head (0: split launch)
+  int bal_min_chunks;      // fewest 32-key chunks a balanced workgroup takes
+  size_t bal_offset;       // workspace bytes before the balanced launch's partials
   size_t workspace_bytes;  // bytes the call needs
   int window;              // sliding window (0 = none): splits cut the window's pages
 };

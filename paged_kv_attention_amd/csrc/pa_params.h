@@ -75,7 +75,19 @@ struct AttnParams {
   const void* new_v;
   const int32_t* new_slots;
   int64_t new_stride_tok, new_stride_head;
+  // balanced 16-row decode tiles (bal_wgs > 0): a grid of (KV head,
+  // bal_wgs) workgroups; wave w = 4 u + (wave index) takes chunks
+  // [w R, (w + 1) R) of the batch's 32-key chunks laid end to end (R =
+  // max(bal_min_chunks, ceil(total / (4 bal_wgs)))); its piece of sequence
+  // b keeps partial slot b + w
+  int32_t bal_wgs, bal_min_chunks;
+  float* bal_acc;           // [(B + 4 bal_wgs) * ws_tok * Hq][D] float32
+  float* bal_ml;            // [(B + 4 bal_wgs) * ws_tok * Hq][2] float32
+  int32_t* bal_meta;        // [B][2]: first partial slot of sequence b, slots (0 or 1: no combine)
 };
+
+// Most sequences a balanced decode launch takes (its prefix sums live in LDS).
+constexpr int bal_max_seqs() { return 512; }
 
 // First page of the split ranges of a sequence with context L and n step
 // tokens: the page of its first token's window start (0 without a window).

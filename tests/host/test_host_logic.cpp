@@ -30,7 +30,32 @@ int main() {
   pa_dims c2 = dims(32, 32, 1, 32, 8, 128, 64, 2000, 64);
   pa::Plan p2 = pa::make_plan(&c2, PA_BF16, 256);
   CHECK(p2.splits == 3 && p2.pages_per_split == 22 && p2.combine && p2.comb_tokens == 1);
+  // splits of 1408 keys: the split launch
+  CHECK(p2.bal_wgs == 0 && p2.ws_splits == 3);
   CHECK(p2.workspace_bytes == (size_t)3 * 32 * 32 * 130 * 4);
+  // the same batch over a table of 16384 positions cuts splits of 5504 keys:
+  // the balanced launch, whose 256 waves of 64 workgroups per KV head share
+  // the batch's chunks; partial slots b + w < 32 + 256 of 32 rows, and two
+  // ints per sequence for the combine
+  pa_dims c2l = dims(32, 32, 1, 32, 8, 128, 64, 8192, 256);
+  pa::Plan p2l = pa::make_plan(&c2l, PA_BF16, 256);
+  CHECK(p2l.splits == 3 && p2l.bal_wgs == 64 && p2l.bal_min_chunks == 4 && p2l.ws_splits == 1 && p2l.bal_offset == 0);
+  CHECK(p2l.workspace_bytes == (size_t)(32 + 256) * 32 * 130 * 4 + 32 * 8);
+  // one sequence keeps the split launch
+  pa_dims c1l = dims(1, 1, 1, 32, 8, 128, 64, 512, 512);
+  CHECK(pa::make_plan(&c1l, PA_BF16, 256).bal_wgs == 0);
+  // an explicit split count keeps the split launch
+  pa_dims c2s = c2;
+  c2s.num_splits = 3;
+  pa::Plan p2s = pa::make_plan(&c2s, PA_BF16, 256);
+  CHECK(p2s.bal_wgs == 0 && p2s.ws_splits == 3 && p2s.workspace_bytes == (size_t)3 * 32 * 32 * 130 * 4);
+  // more sequences than a balanced launch takes (a chip of 1024 CUs would
+  // still split them): split launch
+  pa_dims c2b = dims(513, 513, 1, 32, 1, 128, 64, 2000, 256);
+  pa::Plan p2b = pa::make_plan(&c2b, PA_BF16, 1024);
+  CHECK(p2b.splits > 1 && p2b.bal_wgs == 0);
+  // the float32 path never balances
+  CHECK(pa::make_plan(&c2l, PA_F32, 256).bal_wgs == 0);
   // the same sequences with 2-token steps aim at two workgroups per CU
   pa_dims c2v = dims(32, 64, 2, 32, 8, 128, 64, 2000, 64);
   CHECK(pa::make_plan(&c2v, PA_BF16, 256).splits == 2);
@@ -92,7 +117,10 @@ int main() {
   // decode tiles it takes at least 8 (16 pages each); partials only for the
   // 16 decode-class token slots
   CHECK(p4.splits == 2 && p4.splits_big == 8 && p4.pages_per_split_big == 16 && p4.ws_tok == 16);
-  CHECK(p4.workspace_bytes == (size_t)8 * 32 * 16 * 32 * 130 * 4);
+  // the 16-row tiles run balanced: their partials follow the verify tiles'
+  const size_t w4 = (size_t)8 * 32 * 16 * 32 * 130 * 4;
+  CHECK(p4.bal_wgs == 64 && p4.ws_splits == 8 && p4.bal_offset == w4);
+  CHECK(p4.workspace_bytes == w4 + (size_t)(32 + 256) * 16 * 32 * 130 * 4 + 32 * 8);
   // one sequence's 16-token verify block over 2048 positions: 8 splits of
   // 256 keys (the fewest keys a verify split takes)
   pa_dims v1 = dims(1, 16, 16, 32, 8, 128, 64, 32, 32);
@@ -111,6 +139,7 @@ int main() {
   c5.num_tokens = 3 * 8192 + 1;
   pa::Plan p5b = pa::make_plan(&c5, PA_BF16, 256);
   CHECK(p5b.prefill && p5b.dec_small && p5b.dec_big && p5b.combine);
+  CHECK(p5b.bal_wgs == 0);                       // splits of 512 keys
   CHECK(p5b.workspace_bytes == (size_t)p5b.splits * 4 * 16 * 32 * 130 * 4 && p5b.splits >= p5b.splits_big);
   // two verify blocks of 15 and 15 (bound 16): at least 14 tokens each -> only the big tile
   pa_dims v2 = dims(2, 30, 16, 32, 8, 128, 64, 100, 16);

@@ -109,6 +109,12 @@ def test_workspace_and_split_rules():
     S = lib.pa_choose_splits(ctypes.byref(d))
     assert S == (1 if 32 * 8 >= 2 * cus else min(32, -(-3 * cus // (32 * 8)), 64 // 4))
     assert lib.pa_workspace_size(ctypes.byref(d), 1) == (S * 32 * 32 * 130 * 4 if S > 1 else 0)
+    # over a table of 16384 positions the splits reach 2048 keys and more:
+    # the balanced launch instead, whose partials take slots b + w < 32 +
+    # 4 ceil(2 CUs / 8) (w: a wave) of 32 rows each, plus two ints per sequence
+    d = _dims(num_seqs=32, num_tokens=32, table_width=256, num_pages=8192)
+    U = -(-2 * cus // 8)
+    assert lib.pa_workspace_size(ctypes.byref(d), 1) == (32 + 4 * U) * 32 * 130 * 4 + 32 * 8
     # an explicit count wins (capped at the table width)
     d = _dims(num_splits=3)
     assert lib.pa_choose_splits(ctypes.byref(d)) == 3
