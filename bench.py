@@ -314,7 +314,8 @@ def other_workloads(steps, warmup):
     """The other configurations and the decode shapes the headline leaves out:
     the fp32 single-sequence decode (latency), the ragged decode batch, the
     mixed batch, one long bf16 sequence at 4096 and 32768 positions (one
-    sequence must still fill the chip), and a batch of 16-token verification
+    sequence must still fill the chip), the ragged batch at contexts up to
+    16384 (the balanced decode launch) and a batch of 16-token verification
     steps; each with its HBM roofline.  Pools are rotated so the Infinity
     Cache cannot hold them.  `ms` brackets each call with events (the host's
     launch path included); `gpu_ms` is the GPU time per call with the host
@@ -328,12 +329,20 @@ def other_workloads(steps, warmup):
     verify = make_custom(seed=13, context_lens=[2048] * 64, query_lens=[16] * 64, num_q_heads=32, num_kv_heads=8,
                          head_dim=128, page_size=64, dtype=torch.bfloat16,
                          name="bf16 verification: 64 seqs x 16-token steps at 2048 positions, 32/8 heads, D 128, page 64")
+    # the ragged decode batch at four times the context: splits of 5504 keys,
+    # so the 16-row tiles run as the balanced launch
+    g = torch.Generator().manual_seed(11)
+    long_lens = torch.randint(1, 16385, (32,), generator=g).tolist()
+    ragged_long = make_custom(seed=12, context_lens=long_lens, query_lens=[1] * 32, num_q_heads=32, num_kv_heads=8,
+                              head_dim=128, page_size=64, dtype=torch.bfloat16,
+                              name="bf16 ragged decode, 32 seqs, ctx U{1..16384}, 32/8 heads, D 128, page 64")
     for key, cfg, layers, name in [
             ("config1", 1, 1, "fp32 single-sequence decode, 8/2 heads, D 64, page 16, ctx 600"),
             ("config2", 2, 8, "bf16 ragged decode, 32 seqs, ctx U{1..4096}, 32/8 heads, D 128, page 64"),
             ("config4", 4, 8, "bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify"),
             ("decode_1x4096", one(4096, 11), 32, None),
             ("decode_1x32768", one(32768, 12), 8, None),
+            ("decode_ragged_32x16k", ragged_long, 4, None),
             ("verify_64x16_at_2048", verify, 4, None)]:
         print(f"[bench] other workload {key}: building inputs", file=sys.stderr, flush=True)
         wb = WorkloadBench(cfg, layers)
