@@ -264,7 +264,8 @@ class WorkloadBench:
         dims = pa.make_dims(self.q, self.pools[0][0], self.bt, out=self.out, max_query_len=w.max_query_len,
                             num_splits=num_splits)
         self.ws = torch.empty(max(pa.workspace_size(dims, w.dtype), 16), dtype=torch.uint8, device=dev)
-        self.splits = pa.choose_splits(dims)
+        # pa_choose_splits gives the bf16 count; float32 calls follow their own rule
+        self.splits = pa.choose_splits(dims) if w.dtype != torch.float32 else "float32 rule"
         lens = w.context_lens.tolist()
         e = 4 if w.dtype == torch.float32 else 2
         self.bytes = algorithmic_bytes(lens, w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, ps, e,

@@ -319,7 +319,9 @@ size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn
  * workgroups for two per CU of the current device (three when every sequence
  * has one token, max_query_len == 1, and two are not reached), with at least
  * 128 keys per split and at most 64 splits (page "32. Production attention
- * kernels", How many splits?).  Verification blocks (16 < n*G <= 64 rows)
+ * kernels", How many splits?); this is the count for bf16 pools (float32
+ * calls aim at one workgroup per CU with at least 64 keys per split, at most
+ * 64 splits).  Verification blocks (16 < n*G <= 64 rows)
  * take a count of their own: about two workgroups per CU over the batch's
  * (sequence, KV head) pairs, at least 8 when prefill or decode-row tiles
  * share the batch (the few verification steps of a mixed batch then run

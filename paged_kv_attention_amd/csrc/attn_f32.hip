@@ -278,8 +278,9 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
 // (Long contexts: split the keys) written for unnormalised partials, as in
 // page "Attention and KV Cache" (Split-KV decode, Combine).
 // One 256-thread workgroup per row: the threads form 256 / (D/4) groups,
-// group k takes splits k, k + groups, ... (each thread 4 dims), so a row with
-// many splits costs a few memory latencies rather than one per split.  The
+// group k takes splits k, k + groups, ... (each thread 4 dims), and the
+// first four splits of every group arrive together with their (m, l) pairs,
+// so a row with up to 4 * groups splits costs one memory latency.  The
 // groups' sums are added in LDS in group order, so the result does not
 // depend on scheduling.
 // ---------------------------------------------------------------------------
@@ -287,10 +288,16 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
   constexpr int CPR = D / 4;                     // threads per partial row (4 dims each)
   constexpr int NGR = 256 / CPR;                 // split groups
+  constexpr int BATCH = 4 * NGR;                 // splits whose loads are in flight at once
   __shared__ float red[NGR][D + 4];
   __shared__ float red_m[NGR], red_l[NGR];
   const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int grp = threadIdx.x / CPR, c4 = threadIdx.x % CPR;
+  // the sequence's token range and, after a balanced launch, its partial
+  // slots are requested together
+  const bool bal = p.bal_wgs > 0;
+  i32x2 meta = {0, 0};
+  if (bal) meta = *(const i32x2*)(p.bal_meta + 2 * b);
   const int s0 = p.query_start_loc[b];
   const int n = p.query_start_loc[b + 1] - s0;
   if (t >= n || n > p.comb_max_n) return;
@@ -304,22 +311,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
   int64_t NH = p.ws_flat ? (int64_t)p.num_tokens * p.num_q_heads : (int64_t)p.num_seqs * p.ws_tok * p.num_q_heads;
   int64_t row = p.ws_flat ? (int64_t)tok * p.num_q_heads + h : ((int64_t)b * p.ws_tok + t) * p.num_q_heads + h;
   int s_base = 0;
-  if (p.bal_wgs > 0 && n * p.group <= 16) {
+  if (bal && n * p.group <= 16) {
     // balanced 16-row tiles: the sequence's pieces hold slots s_base ..
     // s_base + S - 1 of ws_tok * Hq rows each (one piece: written by the
     // decode kernel)
-    s_base = p.bal_meta[2 * b];
-    S = p.bal_meta[2 * b + 1];
+    s_base = meta[0];
+    S = meta[1];
     acc_p = p.bal_acc;
     ml_p = p.bal_ml;
     NH = (int64_t)p.ws_tok * p.num_q_heads;
     row = (int64_t)t * p.num_q_heads + h;
   }
   if (S <= 1) return;
-  // this group's maximum, four splits' loads in flight at a time; padding
-  // entries are (-inf, 0) and leave every sum bit for bit unchanged
+  // Group grp takes splits grp, grp + NGR, ...; the first BATCH splits'
+  // (m, l) pairs and partial rows are loaded at once and kept, so a row with
+  // up to BATCH splits costs one memory latency.  Padding entries are
+  // (-inf, 0) and leave every sum bit for bit unchanged.
+  auto load = [&](int s, f32x2 (&ml)[4], f32x4 (&av)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sj = s + j * NGR;
+      if (sj < S) {
+        const int64_t ri = (s_base + sj) * NH + row;
+        ml[j] = *(const f32x2*)(ml_p + ri * 2);
+        av[j] = *(const f32x4*)(acc_p + ri * D + 4 * c4);
+      } else {
+        ml[j] = f32x2{kNegInf, 0.f};
+        av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  f32x2 ml0[4];
+  f32x4 av0[4];
+  load(grp, ml0, av0);
   float M = kNegInf;
-  for (int s = grp; s < S; s += 4 * NGR) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) M = fmaxf(M, ml0[j][0]);
+  for (int s = grp + BATCH; s < S; s += BATCH) {
     float m[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) m[j] = s + j * NGR < S ? ml_p[((s_base + s + j * NGR) * NH + row) * 2] : kNegInf;
@@ -333,21 +361,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
   const float Ms = M == kNegInf ? 0.f : M;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int s = grp; s < S; s += 4 * NGR) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float w = fast_exp2(ml0[j][0] - Ms);
+    l = fmaf(w, ml0[j][1], l);
+    acc += w * av0[j];
+  }
+  for (int s = grp + BATCH; s < S; s += BATCH) {
     f32x2 ml[4];
     f32x4 av[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int sj = s + j * NGR;
-      if (sj < S) {
-        const int64_t ri = (s_base + sj) * NH + row;
-        ml[j] = *(const f32x2*)(ml_p + ri * 2);
-        av[j] = *(const f32x4*)(acc_p + ri * D + 4 * c4);
-      } else {
-        ml[j] = f32x2{kNegInf, 0.f};
-        av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+    load(s, ml, av);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float w = fast_exp2(ml[j][0] - Ms);

@@ -73,11 +73,11 @@ int choose_splits_over(const pa_dims* d, pa_dtype dtype, int cu_count, int W) {
   // faster with two.
   if (dtype == PA_BF16 && mql == 1 && units < target) want = (3 * (int64_t)cu_count + units - 1) / units;
   // at least 128 keys per bf16 split (one 32-key chunk per wave of a 4-wave
-  // workgroup); a float32 split keeps at least 1024 so each of its waves has
-  // chunks to walk (a short context is one launch with no combine); at most
-  // 64 splits, so one sequence with 8 KV heads still reaches two workgroups
-  // per CU
-  const int min_keys = dtype == PA_BF16 ? 128 : 1024;
+  // workgroup) and 64 per float32 split (four 16-key chunks: the 600-key
+  // single-sequence decode measured 15.2 us as one split and 10.4-10.6 us
+  // with 10 to 38 splits and the combine); at most 64 splits, so one
+  // sequence with 8 KV heads still reaches two workgroups per CU
+  const int min_keys = dtype == PA_BF16 ? 128 : 64;
   const int min_pages = (min_keys + d->page_size - 1) / d->page_size;
   const int64_t cap_pages = (W + min_pages - 1) / min_pages;
   int64_t s = want;

@@ -40,7 +40,7 @@ pa_status check_dims(const pa_dims* d, pa_dtype dtype);
 
 // Split count from host scalars only: bf16 aims at about two workgroups per
 // CU with at least 128 keys per split, float32 at one workgroup per CU with
-// at least 1024 keys per split; at most 64 splits; an explicit
+// at least 64 keys per split; at most 64 splits; an explicit
 // dims->num_splits > 0 wins (capped at W).
 int choose_splits(const pa_dims* d, pa_dtype dtype, int cu_count);
 // The same rule over W pages instead of the table width.

@@ -157,14 +157,20 @@ int main() {
   pa_dims g32 = dims(2, 2, 1, 64, 2, 128, 64, 100, 16);
   pa::Plan pg = pa::make_plan(&g32, PA_BF16, 256);
   CHECK(pg.dec_max_n == 2 && !pg.dec_small && pg.dec_big && pg.big_nt == 2);
-  // float32: a 600-key context is one split of one 16-row tile (no combine);
-  // a long one is cut into splits of at least 1024 keys
+  // float32: a 600-key context (38 pages of 16) is cut into splits of at
+  // least 64 keys, 4 pages: 10 splits of one 16-row tile and the combine;
+  // a long one into at most 64 splits
   pa_dims c1 = dims(1, 1, 1, 8, 2, 64, 16, 64, 38);
   pa::Plan p1 = pa::make_plan(&c1, PA_F32, 256);
-  CHECK(p1.splits == 1 && !p1.combine && p1.num_qtiles == 1 && p1.workspace_bytes == 0);
+  CHECK(p1.splits == 10 && p1.pages_per_split == 4 && p1.combine && p1.num_qtiles == 1);
+  CHECK(p1.workspace_bytes == (size_t)10 * 1 * 1 * 8 * 66 * 4);
   pa_dims l1 = dims(1, 1, 1, 8, 2, 64, 16, 2048, 2048);   // 32768 keys
   pa::Plan pl1 = pa::make_plan(&l1, PA_F32, 256);
-  CHECK(pl1.splits == 32 && pl1.pages_per_split == 64 && pl1.combine && pl1.comb_tokens == 1);
+  CHECK(pl1.splits == 64 && pl1.pages_per_split == 32 && pl1.combine && pl1.comb_tokens == 1);
+  // a context of 64 keys or fewer stays one split with no combine
+  pa_dims s1 = dims(1, 1, 1, 8, 2, 64, 16, 64, 4);
+  pa::Plan ps1 = pa::make_plan(&s1, PA_F32, 256);
+  CHECK(ps1.splits == 1 && !ps1.combine && ps1.workspace_bytes == 0);
   pa_dims f5 = dims(2, 10, 5, 8, 2, 64, 16, 64, 38);      // 5 tokens x group 4: two 16-row tiles
   CHECK(pa::make_plan(&f5, PA_F32, 256).num_qtiles == 2);
   c1.num_splits = 38;
