@@ -284,6 +284,8 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
 // groups' sums are added in LDS in group order, so the result does not
 // depend on scheduling.
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(2))) int32_t i32x2;
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
   constexpr int CPR = D / 4;                     // threads per partial row (4 dims each)
