@@ -35,7 +35,8 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
 # the context are zero-filled or masked to -inf): without NaN semantics fmaxf
 # maps to a bare v_max/v_max3 instead of quieting each operand first.
 # Infinities keep their IEEE meaning (the masks rely on -inf).
-FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"], "prefill16.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"], "prefill16.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
+              "mixed.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):

@@ -26,6 +26,9 @@ static hipError_t launch_verify(const AttnParams& p, int big_nt, hipStream_t st)
 }
 hipError_t launch_f32(const AttnParams& p, hipStream_t st);
 hipError_t launch_combine(const AttnParams& p, bool bf16, hipStream_t st);
+bool mixed_supported(int head_dim);
+hipError_t launch_mixed(const AttnParams& pp, bool have_pre, const AttnParams& pv, bool have_ver,
+                        const AttnParams& pd, bool have_dec, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
 hipError_t launch_kv_write_quant(const KvWriteParams& p, hipStream_t st);
 
@@ -400,6 +403,29 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
     // first.
     const bool fuse = wp.num_tokens > 0 && classes == 1 && pl.dec_small && pl.bal_wgs == 0;
     if (wp.num_tokens > 0 && !fuse && launch_kv_write(wp, s) != hipSuccess) return PA_ERR_LAUNCH;
+#ifndef PA_MIXED
+#define PA_MIXED 1
+#endif
+    // A batch of several classes over bf16 pools with 128-dim heads whose
+    // prefill (if any) takes 64-row tiles runs as one launch of all its
+    // tiles, then the combine, on the caller's stream.  A balanced decode
+    // class there takes about one workgroup per CU (its partial slots stay
+    // within the planned ones): the mixed batch measured 150 us with the
+    // three launches on forked streams, 148 us as one launch with the
+    // prefill tiles first and two decode workgroups per CU, 144 us with the
+    // decode tiles first, and 130-135 us with the decode tiles first at
+    // 0.75-1.25 workgroups per CU.
+    if (PA_MIXED && classes >= 2 && !kq && mixed_supported(dims->head_dim) &&
+        (!pl.prefill || prefill_small_tiles(dims, cu_count()))) {
+      AttnParams pp = p;
+      pp.tok_per_tile = 64 / p.group;
+      pp.num_qtiles = (pl.mql + pp.tok_per_tile - 1) / pp.tok_per_tile;
+      AttnParams qd = q1;
+      if (qd.bal_wgs > 0) qd.bal_wgs = (cu_count() + p.num_kv_heads - 1) / p.num_kv_heads;
+      e = launch_mixed(pp, pl.prefill, q2, pl.dec_big, qd, pl.dec_small, s);
+      if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
+      return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
     // The side streams are made on the first bf16 call of any kind: HIP deals
     // streams to the process's few hardware queues in the order they are
     // created, and side streams that share a queue with the caller's stream
