@@ -43,12 +43,15 @@ CSRC = os.path.join(ROOT, "paged_kv_attention_amd", "csrc")
 # Measured HBM traffic per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
 # a plain copy's counts) is kept next to the hash of the sources it was taken
 # from; a kernel changed since then reports traffic null.
-TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.json"), "decode.hip"),
-                 "prefill": (os.path.join(ROOT, "profiles", "prefill_c5_traffic.json"), "prefill.hip"),
-                 "prefill_d256": (os.path.join(ROOT, "profiles", "prefill_c6_traffic.json"), "prefill16.hip")}
+TRAFFIC_FILES = {"decode": (os.path.join(ROOT, "profiles", "decode_c3_traffic.json"), ("decode.hip", "decode_tile.h")),
+                 "prefill": (os.path.join(ROOT, "profiles", "prefill_c5_traffic.json"), ("prefill.hip",)),
+                 "prefill_d256": (os.path.join(ROOT, "profiles", "prefill_c6_traffic.json"),
+                                  ("prefill16.hip", "prefill16_tile.h")),
+                 "mixed": (os.path.join(ROOT, "profiles", "mixed_c4_traffic.json"),
+                           ("mixed.hip", "decode_tile.h", "prefill16_tile.h"))}
 # kernel (name prefix, with its head-dim template argument) each traffic file is about
 TRAFFIC_KERNELS = {"decode": "pa::decode_splitkv_kernel<128, 1,", "prefill": "pa::prefill_kernel<128,",
-                   "prefill_d256": "pa::prefill16_kernel<256, 8, false, 0>"}
+                   "prefill_d256": "pa::prefill16_kernel<256, 8, false, 0>", "mixed": "pa::mixed_kernel<"}
 
 
 # ----------------------------------------------------------------------------- accounting
@@ -100,10 +103,10 @@ def kv_write_bytes(tokens, num_kv_heads, head_dim, elem_bytes):
     return 2 * 2 * tokens * num_kv_heads * head_dim * elem_bytes + 4 * tokens
 
 
-def kernel_src_hash(kernel_file):
-    """Hash of a kernel's source and the device headers it includes."""
+def kernel_src_hash(kernel_files):
+    """Hash of a kernel's sources and the device headers it includes."""
     h = hashlib.sha256()
-    for name in (kernel_file, "pa_device.h", "pa_params.h"):
+    for name in (*kernel_files, "pa_device.h", "pa_params.h"):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -348,6 +351,9 @@ def other_workloads(steps, warmup):
         print(f"[bench] other workload {key}: building inputs", file=sys.stderr, flush=True)
         wb = WorkloadBench(cfg, layers)
         res[key] = _hbm_entry(name or wb.w.name, wb, steps, warmup, layers)
+        if key == "config4":
+            # the mixed batch is one launch (and the combine): its measured HBM bytes
+            res[key]["roofline"]["traffic"] = measured_traffic("mixed")
         del wb
         torch.cuda.empty_cache()
     return res
@@ -696,7 +702,7 @@ def traffic_summary(which, fetch_csv, write_csv):
     wk = [r[2] for r in write if r[1].startswith(kname) or ("void " + kname) in r[1]]
     fb = sum(fk) / len(fk) * 1024 * f_scale
     wb = sum(wk) / len(wk) * 1024 * w_scale
-    cfg = {"decode": 3, "prefill": 5, "prefill_d256": 6}[which]
+    cfg = {"decode": 3, "prefill": 5, "prefill_d256": 6, "mixed": 4}[which]
     w = make(cfg)
     alg = algorithmic_bytes(w.context_lens.tolist(), w.query_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
                             w.page_size, 2)
@@ -712,7 +718,7 @@ def traffic_summary(which, fetch_csv, write_csv):
              f"WRITE_SIZE per dispatch (KiB): {[round(x, 1) for x in wk]}",
              f"scaled traffic per launch: fetch {int(fb)} B + write {int(wb)} B = {int(fb + wb)} B",
              f"algorithmic bytes per launch: {alg} B -> traffic / algorithmic = {(fb + wb) / alg:.4f}",
-             f"source hash ({src} + pa_device.h + pa_params.h, sha256[:16]): {rec['src_sha256_16']}"]
+             f"source hash ({' + '.join(src)} + pa_device.h + pa_params.h, sha256[:16]): {rec['src_sha256_16']}"]
     return "\n".join(lines)
 
 
@@ -807,7 +813,7 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other measured workloads")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay of the decode step")
     ap.add_argument("--no-variants", action="store_true", help="skip the sliding-window / sink workloads")
-    ap.add_argument("--only", choices=["decode", "prefill", "prefill_d256"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_d256", "mixed"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--trace-summary", metavar="DB", default=None,
                     help="print per-kernel durations from a rocprofv3 results database and exit")
@@ -940,6 +946,18 @@ def main():
             result[leg] = pre
         del pb
         torch.cuda.empty_cache()
+
+    if args.only == "mixed":
+        # the mixed batch alone (its one launch and the combine), for profiler runs
+        print("[bench] mixed batch: building inputs", file=sys.stderr, flush=True)
+        wb = WorkloadBench(4, 8)
+        entry = _hbm_entry("bf16 mixed batch: 512-token chunk over 1024 prefix + 30 decodes + 5-token verify", wb,
+                           args.steps, args.warmup, 8)
+        result.update({"metric": METRIC, "value": entry["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                       "warmup": args.warmup, "ms_per_step": entry["gpu_ms"], "higher_is_better": True,
+                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                       "config": {"workload": entry["workload"]},
+                       "roofline": dict(entry["roofline"], traffic=measured_traffic("mixed"))})
 
     if args.only is None and not args.no_others:
         result["other_workloads"] = other_workloads(args.steps, args.warmup)
