@@ -4,13 +4,15 @@
 // the events that fork and join them (page "32. Production attention
 // kernels", One kernel for the whole batch: one launch serves every sequence
 // class).  The flat workgroup index picks the class: decode tiles first, so
-// they are dealt to the CUs before anything else (a balanced decode launch
-// here has about one workgroup per CU, whose four waves stream the batch's
-// K/V from the start while the CU's other workgroup slot takes the prefill
-// and verification tiles), then prefill tiles (heaviest first inside their
-// range), then verification tiles.  Each workgroup runs the same tile code
-// as the class's own kernel, with the class's argument block.  Classes
-// without sequences have no workgroups.
+// they are dealt to the CUs before anything else, then prefill tiles
+// (heaviest first inside their range), then verification tiles.  Beside a
+// prefill class a balanced decode launch has about one workgroup per CU
+// dealt first, whose four waves stream the batch's K/V from the start while
+// the CU's other slot takes the prefill and verification tiles, and, when
+// the prefill tiles fit one per CU, as many again dealt last, which take
+// half as many chunks each and fill the slots the other tiles leave.  Each
+// workgroup runs the same tile code as the class's own kernel, with the
+// class's argument block.  Classes without sequences have no workgroups.
 #include "decode_tile.h"
 #include "prefill16_tile.h"
 
@@ -29,10 +31,14 @@ void mixed_kernel(const AttnParams pp, const AttnParams pv, const AttnParams pd,
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) char smem[MixedLds<D>::BYTES];
   PA_LDS char* lds = (PA_LDS char*)smem;
-  // decode tiles take the first workgroups of the grid; f is the index in
-  // the order prefill, verification, decode that the argument counts use
+  // the decode tiles take the first workgroups of the grid (a balanced
+  // launch with bal_early > 0: its early workgroups first, the others last);
+  // f is the index in the order prefill, verification, decode that the
+  // argument counts use
   const int n_dec = (int)gridDim.x - n_pre - n_ver;
-  const int f = (int)blockIdx.x < n_dec ? n_pre + n_ver + (int)blockIdx.x : (int)blockIdx.x - n_dec;
+  const int n_first = BAL && pd.bal_early > 0 ? pd.bal_early * pd.num_kv_heads : n_dec;
+  const int bi = (int)blockIdx.x;
+  const int f = bi < n_first ? n_pre + n_ver + bi : bi < n_first + n_pre + n_ver ? bi - n_first : bi;
   if (f < n_pre) {
     prefill16_tile<D, 4, WIN, T16_PREFILL>(pp, lds, f, 0, 0, n_pre);
   } else if (f < n_pre + n_ver) {
