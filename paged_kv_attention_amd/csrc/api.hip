@@ -392,7 +392,7 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
       if (!kq && prefill_small_tiles(dims, cu_count())) {
         AttnParams pp = p;
         pp.tok_per_tile = 64 / p.group;
-        pp.num_qtiles = (pl.mql + pp.tok_per_tile - 1) / pp.tok_per_tile;
+        pp.num_qtiles = prefill_small_slots(dims->num_tokens, dims->num_seqs, pl.mql, pp.tok_per_tile, pl.dec_max_n);
         return launch_prefill16_small(pp, st);
       }
       return launch_prefill(p, st);
@@ -409,31 +409,20 @@ static pa_status attention_impl(const void* q, const void* k_pool, const void* v
     // A batch of several classes over bf16 pools with 128-dim heads whose
     // prefill (if any) takes 64-row tiles runs as one launch of all its
     // tiles, then the combine, on the caller's stream.  Beside a prefill
-    // class a balanced decode class takes about one workgroup per CU dealt
-    // first, and when the prefill's tiles fit one per CU as many again dealt
-    // last with half the chunks each (its partial slots stay within the
-    // planned ones).  The mixed batch measured 150 us with the three
-    // launches on forked streams, 148 us as one launch with the prefill
-    // tiles first and two decode workgroups per CU, 144 us with the decode
-    // tiles first, 130-135 us with the decode tiles first at 0.75-1.25
-    // workgroups per CU, and 129-131 us with the later half-size workgroups.
+    // class a balanced decode class takes about one workgroup per CU (its
+    // partial slots stay within the planned ones).  The mixed batch measured
+    // 150 us with the three launches on forked streams, 148 us as one launch
+    // with the prefill tiles first and two decode workgroups per CU, 144 us
+    // with the decode tiles first, 130-135 us with the decode tiles first at
+    // 0.75-1.25 workgroups per CU, and 122-125 us with the prefill tiles in a
+    // compact grid (67 slots per KV head instead of 1,024).
     if (PA_MIXED && classes >= 2 && !kq && mixed_supported(dims->head_dim) &&
         (!pl.prefill || prefill_small_tiles(dims, cu_count()))) {
       AttnParams pp = p;
       pp.tok_per_tile = 64 / p.group;
-      pp.num_qtiles = (pl.mql + pp.tok_per_tile - 1) / pp.tok_per_tile;
+      pp.num_qtiles = prefill_small_slots(dims->num_tokens, dims->num_seqs, pl.mql, pp.tok_per_tile, pl.dec_max_n);
       AttnParams qd = q1;
-      if (qd.bal_wgs > 0 && pl.prefill) {
-        const int per_cu = (cu_count() + p.num_kv_heads - 1) / p.num_kv_heads;
-        const int64_t pre_tiles = (int64_t)pp.num_qtiles * p.num_kv_heads;
-        if (pre_tiles <= cu_count() && 2 * per_cu <= pl.bal_wgs) {
-          qd.bal_early = per_cu;
-          qd.bal_wgs = 2 * per_cu;
-          qd.bal_late_w16 = 8;
-        } else {
-          qd.bal_wgs = per_cu;
-        }
-      }
+      if (qd.bal_wgs > 0 && pl.prefill) qd.bal_wgs = (cu_count() + p.num_kv_heads - 1) / p.num_kv_heads;
       e = launch_mixed(pp, pl.prefill, q2, pl.dec_big, qd, pl.dec_small, s);
       if (e == hipSuccess && pl.combine) e = launch_combine(p, true, s);
       return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

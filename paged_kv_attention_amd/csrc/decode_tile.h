@@ -193,26 +193,18 @@ __device__ __attribute__((always_inline)) void decode_tile(const AttnParams& p, 
     qs[2 * tid] = ex;
     qs[2 * tid + 1] = ex + max(cnt[0], 0);
     __syncthreads();
-    // ne early waves take runs of R chunks, nl later ones runs of Rl
-    // (about w16 / 16 of R); the runs lie end to end in wave order
-    const int E = p.bal_early > 0 ? p.bal_early : p.bal_wgs;
-    const int ne = 4 * E, nl = 4 * (p.bal_wgs - E);
-    const int w16 = p.bal_late_w16 > 0 ? p.bal_late_w16 : 16;
-    const int64_t den = (int64_t)ne * 16 + (int64_t)nl * w16;
-    const int R = max(p.bal_min_chunks, (int)(((int64_t)total * 16 + den - 1) / den));
-    const int Rl = max(1, (R * w16 + 15) / 16);
-    const int split_c = ne * R;                 // chunks of the early waves
-    auto run_of = [&](int c) { return c < split_c ? c / R : ne + (c - split_c) / Rl; };   // chunk -> wave
+    const int nw = 4 * p.bal_wgs;               // waves per KV head
+    const int R = max(p.bal_min_chunks, (total + nw - 1) / nw);
     bal_u = 4 * bal_u + wave;                   // from here on: the wave's index
-    bal_lo = min(bal_u < ne ? bal_u * R : split_c + (bal_u - ne) * Rl, total);
-    bal_hi = min(bal_lo + (bal_u < ne ? R : Rl), total);
+    bal_lo = min(bal_u * R, total);
+    bal_hi = min(bal_lo + R, total);
     // for the combine: the first partial slot of each sequence and how many
     // pieces it has (0 or 1: no partials)
     if (g == 0 && by == 0)
       for (int bb = tid; bb < B; bb += 256) {
         const int c = cs[bb], q = qs[bb];
-        p.bal_meta[2 * bb] = bb + run_of(q);
-        p.bal_meta[2 * bb + 1] = c > 0 ? run_of(q + c - 1) - run_of(q) + 1 : 0;
+        p.bal_meta[2 * bb] = bb + q / R;
+        p.bal_meta[2 * bb + 1] = c > 0 ? (q + c - 1) / R - q / R + 1 : 0;
       }
     // rows of a sequence of this launch without any key are zero
     if (by == 0) {

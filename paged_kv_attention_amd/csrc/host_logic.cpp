@@ -251,6 +251,18 @@ bool prefill_small_tiles(const pa_dims* d, int cu_count) {
   return 2 * tiles < (int64_t)cu_count;
 }
 
+int prefill_small_slots(int num_tokens, int num_seqs, int mql, int tpt, int dec_max_n) {
+  if (num_tokens <= 0 || num_seqs <= 0 || tpt < 1) return 1;
+  int64_t nseq = (int64_t)num_tokens / ((int64_t)dec_max_n + 1);
+  if (nseq > num_seqs) nseq = num_seqs;
+  if (nseq < 1) nseq = 1;
+  const int64_t per_seq = ((int64_t)(mql > 0 ? mql : num_tokens) + tpt - 1) / tpt;
+  int64_t slots = ((int64_t)num_tokens + tpt - 1) / tpt + nseq;
+  if (slots > per_seq * nseq) slots = per_seq * nseq;
+  if (slots < 1) slots = 1;
+  return slots > INT_MAX / 2 ? INT_MAX / 2 : (int)slots;
+}
+
 pa_status validate_shared_prefix(const int32_t* bt, const int32_t* lens, const int32_t* qsl, int prefix_len,
                                  const pa_dims* d) {
   if (prefix_len <= 0) return PA_OK;

@@ -74,6 +74,13 @@ CascadePlan make_cascade_plan(const pa_dims* d, pa_dtype dtype, int cu_count, in
 // tiles than half the CUs, the smaller tiles spread the work over the chip.
 bool prefill_small_tiles(const pa_dims* d, int cu_count);
 
+// Tile slots per KV head of the compact grid of 64-row prefill tiles
+// (tpt tokens each): a bound from host scalars on the batch's prefill tiles.
+// A prefill sequence has more than dec_max_n tokens, so there are at most
+// min(B, N / (dec_max_n + 1)) of them, and their tiles number at most
+// ceil(N / tpt) plus one per sequence, and at most ceil(mql / tpt) each.
+int prefill_small_slots(int num_tokens, int num_seqs, int mql, int tpt, int dec_max_n);
+
 // Shared-prefix contract on copied metadata: table rows agree with row 0 on
 // the prefix's pages and every query token sits after the prefix.
 pa_status validate_shared_prefix(const int32_t* block_tables, const int32_t* context_lens,

@@ -4,15 +4,14 @@
 // the events that fork and join them (page "32. Production attention
 // kernels", One kernel for the whole batch: one launch serves every sequence
 // class).  The flat workgroup index picks the class: decode tiles first, so
-// they are dealt to the CUs before anything else, then prefill tiles
-// (heaviest first inside their range), then verification tiles.  Beside a
-// prefill class a balanced decode launch has about one workgroup per CU
-// dealt first, whose four waves stream the batch's K/V from the start while
-// the CU's other slot takes the prefill and verification tiles, and, when
-// the prefill tiles fit one per CU, as many again dealt last, which take
-// half as many chunks each and fill the slots the other tiles leave.  Each
-// workgroup runs the same tile code as the class's own kernel, with the
-// class's argument block.  Classes without sequences have no workgroups.
+// they are dealt to the CUs before anything else, then prefill tiles (a
+// compact grid of the batch's tiles, heaviest first inside a sequence), then
+// verification tiles.  Beside a prefill class a balanced decode launch has
+// about one workgroup per CU, whose four waves stream the batch's K/V from
+// the start while the CU's other slot takes the prefill and verification
+// tiles.  Each workgroup runs the same tile code as the class's own kernel,
+// with the class's argument block.  Classes without sequences have no
+// workgroups.
 #include "decode_tile.h"
 #include "prefill16_tile.h"
 
@@ -31,14 +30,10 @@ void mixed_kernel(const AttnParams pp, const AttnParams pv, const AttnParams pd,
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) char smem[MixedLds<D>::BYTES];
   PA_LDS char* lds = (PA_LDS char*)smem;
-  // the decode tiles take the first workgroups of the grid (a balanced
-  // launch with bal_early > 0: its early workgroups first, the others last);
-  // f is the index in the order prefill, verification, decode that the
-  // argument counts use
+  // decode tiles take the first workgroups of the grid; f is the index in
+  // the order prefill, verification, decode that the argument counts use
   const int n_dec = (int)gridDim.x - n_pre - n_ver;
-  const int n_first = BAL && pd.bal_early > 0 ? pd.bal_early * pd.num_kv_heads : n_dec;
-  const int bi = (int)blockIdx.x;
-  const int f = bi < n_first ? n_pre + n_ver + bi : bi < n_first + n_pre + n_ver ? bi - n_first : bi;
+  const int f = (int)blockIdx.x < n_dec ? n_pre + n_ver + (int)blockIdx.x : (int)blockIdx.x - n_dec;
   if (f < n_pre) {
     prefill16_tile<D, 4, WIN, T16_PREFILL>(pp, lds, f, 0, 0, n_pre);
   } else if (f < n_pre + n_ver) {
@@ -66,7 +61,7 @@ bool mixed_supported(int head_dim) { return head_dim == 128; }
 hipError_t launch_mixed(const AttnParams& pp, bool have_pre, const AttnParams& pv, bool have_ver,
                         const AttnParams& pd, bool have_dec, hipStream_t st) {
   if (pd.head_dim != 128) return hipErrorInvalidValue;
-  const int64_t n_pre = have_pre ? (int64_t)pp.num_qtiles * pp.num_kv_heads * pp.num_seqs : 0;
+  const int64_t n_pre = have_pre ? (int64_t)pp.num_qtiles * pp.num_kv_heads : 0;   // compact tile slots
   const int64_t n_ver = have_ver ? (int64_t)pv.num_splits * pv.num_kv_heads * pv.num_seqs : 0;
   const bool bal = have_dec && pd.bal_wgs > 0;
   const int64_t n_dec = !have_dec ? 0

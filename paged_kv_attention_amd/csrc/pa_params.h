@@ -76,15 +76,11 @@ struct AttnParams {
   const int32_t* new_slots;
   int64_t new_stride_tok, new_stride_head;
   // balanced 16-row decode tiles (bal_wgs > 0): a grid of (KV head,
-  // bal_wgs) workgroups; wave w = 4 u + (wave index) takes a run of R
-  // consecutive chunks of the batch's 32-key chunks laid end to end (R =
+  // bal_wgs) workgroups; wave w = 4 u + (wave index) takes chunks
+  // [w R, (w + 1) R) of the batch's 32-key chunks laid end to end (R =
   // max(bal_min_chunks, ceil(total / (4 bal_wgs)))); its piece of sequence
-  // b keeps partial slot b + w.  With bal_early > 0 the workgroups u <
-  // bal_early are dealt first and the others after other tiles of the same
-  // launch: a later wave's run is bal_late_w16 / 16 of an early wave's
-  // (rounded up), R chosen so that all runs cover the chunks.
+  // b keeps partial slot b + w
   int32_t bal_wgs, bal_min_chunks;
-  int32_t bal_early, bal_late_w16;
   float* bal_acc;           // [(B + 4 bal_wgs) * ws_tok * Hq][D] float32
   float* bal_ml;            // [(B + 4 bal_wgs) * ws_tok * Hq][2] float32
   int32_t* bal_meta;        // [B][2]: first partial slot of sequence b, slots (0 or 1: no combine)

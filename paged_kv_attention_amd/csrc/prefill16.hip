@@ -24,7 +24,7 @@ hipError_t launch_prefill16(const AttnParams& p, hipStream_t st) {
 // A short prefill (few 256-row tiles for the chip) over 64-row tiles,
 // 128-dim heads; p.tok_per_tile and p.num_qtiles describe 64-row tiles.
 hipError_t launch_prefill16_small(const AttnParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)p.num_qtiles * p.num_kv_heads * p.num_seqs));
+  const dim3 grid((unsigned)((int64_t)p.num_qtiles * p.num_kv_heads));   // compact tile slots
   if (p.head_dim != 128) return hipErrorInvalidValue;
   if (p.window > 0) hipLaunchKernelGGL((prefill16_kernel<128, 4, true, T16_PREFILL>), grid, dim3(256), 0, st, p);
   else hipLaunchKernelGGL((prefill16_kernel<128, 4, false, T16_PREFILL>), grid, dim3(256), 0, st, p);

@@ -93,14 +93,44 @@ __device__ __attribute__((always_inline)) void prefill16_tile(const AttnParams& 
     qt = rest / p.num_kv_heads;
     b = 0;
   } else if constexpr (NW == 4) {
-    // 64-row tiles of a short prefill: consecutive tiles go to different
-    // XCDs (the chip's CUs rather than one XCD's L2), heaviest first
-    const int nqt = p.num_qtiles;
-    const int id = bx;
-    qt = nqt - 1 - id % nqt;
-    const int rest = id / nqt;
-    g = rest % p.num_kv_heads;
-    b = rest / p.num_kv_heads;
+    // 64-row tiles of short prefills, in a compact grid: p.num_qtiles tile
+    // slots per KV head (a host bound on the batch's prefill tiles), slot j
+    // the j-th tile of the batch's prefill sequences in sequence order,
+    // heaviest first inside a sequence; consecutive slots go to different
+    // XCDs (the chip's CUs rather than one XCD's L2).  Every wave finds its
+    // slot's sequence by the same scan over the step lengths, 64 sequences
+    // at a time; a slot past the batch's tiles has nothing to do.
+    const int T = p.num_qtiles, TPTs = p.tok_per_tile;
+    const int j = bx % T;
+    g = bx / T;
+    const int ln = threadIdx.x & 63;
+    b = -1;
+    int base = 0;
+    for (int q0 = 0; q0 < p.num_seqs; q0 += 64) {
+      const int sq = q0 + ln;
+      int c = 0;
+      if (sq < p.num_seqs) {
+        const int nq = p.query_start_loc[sq + 1] - p.query_start_loc[sq];
+        c = nq > p.dec_max_n ? (nq + TPTs - 1) / TPTs : 0;
+      }
+      int inc = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (ln >= o) inc += v;
+      }
+      const int tot = __builtin_amdgcn_readlane(inc, 63);
+      if (j < base + tot) {
+        const int at = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + inc > j));   // lane holding tile j
+        const int cb = __builtin_amdgcn_readlane(c, at);
+        const int before = base + __builtin_amdgcn_readlane(inc, at) - cb;
+        b = q0 + at;
+        qt = cb - 1 - (j - before);
+        break;
+      }
+      base += tot;
+    }
+    if (b < 0) return;
   } else {
     // consecutive logical tiles share an XCD; the heaviest tile of a
     // sequence first

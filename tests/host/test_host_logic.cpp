@@ -86,6 +86,15 @@ int main() {
   CHECK(!pa::prefill_small_tiles(&pf, 256));
   pa_dims m256 = dims(32, 547, 512, 16, 4, 256, 64, 4096, 128);
   CHECK(!pa::prefill_small_tiles(&m256, 256));                                // 128-dim heads only
+  // compact grid of 64-row prefill tiles (16 tokens at group 4): the mixed
+  // batch's 547 tokens over 32 sequences (at most 32 prefill sequences of
+  // more than 16 tokens) give ceil(547 / 16) + 32 = 67 slots per KV head;
+  // one 8192-token prompt 512 + 1; a bound never above B * ceil(mql / 16)
+  CHECK(pa::prefill_small_slots(547, 32, 512, 16, 16) == 67);
+  CHECK(pa::prefill_small_slots(8192, 1, 8192, 16, 16) == 512);
+  CHECK(pa::prefill_small_slots(40, 2, 20, 16, 16) == 4);        // two 20-token steps: 2 tiles each
+  CHECK(pa::prefill_small_slots(17, 1, 17, 16, 16) == 2);
+  CHECK(pa::prefill_small_slots(0, 4, 8, 16, 16) == 1);
   pa_dims p2k = dims(1, 2048, 2048, 32, 8, 128, 64, 64, 64);
   CHECK(!pa::prefill_small_tiles(&p2k, 256));                                 // 32 x 8 = 256 tiles
   // 64-dim heads keep the 256-row prefill tiles, about half the CUs busy
