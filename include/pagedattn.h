@@ -323,7 +323,7 @@ size_t pa_workspace_size_opts(const pa_dims* dims, pa_dtype dtype, const pa_attn
  * calls aim at one workgroup per CU with at least 64 keys per split, at most
  * 64 splits).  Verification blocks (16 < n*G <= 64 rows)
  * take a count of their own: about two workgroups per CU over the batch's
- * (sequence, KV head) pairs, at least 8 when prefill or decode-row tiles
+ * (sequence, KV head) pairs, at least 16 when prefill or decode-row tiles
  * share the batch (the few verification steps of a mixed batch then run
  * short key loops), with at least 256 keys per split and at most 64;
  * dims->num_splits, when > 0, sets both counts.  Returns 1 for invalid dims.

@@ -134,9 +134,10 @@ Plan make_plan(const pa_dims* d, pa_dtype dtype, int cu_count, int window) {
       const int min_pages = (256 + d->page_size - 1) / d->page_size;
       const int64_t cap_pages = (W + min_pages - 1) / min_pages;
       // Beside prefill or 16-row decode tiles the verification steps are
-      // likely few, and their key loops run while the other launches hold
-      // the chip: at least 8 splits keep those loops short.
-      if ((pl.prefill || pl.dec_small) && want < 8) want = 8;
+      // likely few, and their key loops run while the other tiles hold the
+      // chip: at least 16 splits keep those loops short (the mixed batch as
+      // one launch: 4, 8, 16, 32 splits measured 138, 124, 119, 120 us).
+      if ((pl.prefill || pl.dec_small) && want < 16) want = 16;
       if (want > 64) want = 64;
       if (want > cap_pages) want = cap_pages;
       if (want < 1) want = 1;

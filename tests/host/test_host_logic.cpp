@@ -123,12 +123,12 @@ int main() {
   CHECK(p4.dec_max_n == 16 && p4.comb_max_n == 16);
   // the verify-tile launch would aim at two workgroups per CU over the 32 x 8
   // (sequence, KV head) pairs (2 splits), but beside the prefill and 16-row
-  // decode tiles it takes at least 8 (16 pages each); partials only for the
+  // decode tiles it takes at least 16 (8 pages each); partials only for the
   // 16 decode-class token slots
-  CHECK(p4.splits == 2 && p4.splits_big == 8 && p4.pages_per_split_big == 16 && p4.ws_tok == 16);
+  CHECK(p4.splits == 2 && p4.splits_big == 16 && p4.pages_per_split_big == 8 && p4.ws_tok == 16);
   // the 16-row tiles run balanced: their partials follow the verify tiles'
-  const size_t w4 = (size_t)8 * 32 * 16 * 32 * 130 * 4;
-  CHECK(p4.bal_wgs == 64 && p4.ws_splits == 8 && p4.bal_offset == w4);
+  const size_t w4 = (size_t)16 * 32 * 16 * 32 * 130 * 4;
+  CHECK(p4.bal_wgs == 64 && p4.ws_splits == 16 && p4.bal_offset == w4);
   CHECK(p4.workspace_bytes == w4 + (size_t)(32 + 256) * 16 * 32 * 130 * 4 + 32 * 8);
   // one sequence's 16-token verify block over 2048 positions: 8 splits of
   // 256 keys (the fewest keys a verify split takes)
