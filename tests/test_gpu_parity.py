@@ -321,3 +321,27 @@ def test_config5_prefill_every_row(config):
     w = make(config)
     got = run_lib(w, out_fill=float("nan"))
     check_every_row(w, got, label=f"C{config} every row")
+
+
+def test_compact_prefill_grid_many_sequences():
+    # The 64-row prefill tiles of a short prefill take a compact grid whose
+    # slots each wave maps to (sequence, tile) by a scan of the step lengths,
+    # 64 sequences at a time.  150 sequences (three scan chunks) with prefill
+    # steps of 17-150 tokens in every chunk, among decodes and verification
+    # steps: as one launch of all classes (mixed batch), and as prefill
+    # alone over the same kind of spread.
+    g = torch.Generator().manual_seed(31)
+    qlens, lens = [], []
+    for b in range(150):
+        r = int(torch.randint(0, 6, (1,), generator=g))
+        n = 1 if r < 3 else int(torch.randint(2, 6, (1,), generator=g)) if r == 3 else int(torch.randint(17, 151, (1,), generator=g))
+        qlens.append(n)
+        lens.append(n + int(torch.randint(0, 400, (1,), generator=g)))
+    qlens[0], qlens[63], qlens[64], qlens[127], qlens[128], qlens[149] = 40, 17, 100, 150, 33, 64
+    lens[0], lens[63], lens[64], lens[127], lens[128], lens[149] = 40, 300, 100, 500, 33, 64
+    w = poison_unused(_custom(120, lens, qlens))
+    got = run_lib(w, out_fill=float("nan"))
+    check(w, got, label="compact prefill grid, 150 sequences, mixed")
+    pre = [i for i, n in enumerate(qlens) if n > 16]
+    wp = poison_unused(_custom(121, [lens[i] for i in pre], [qlens[i] for i in pre]))
+    check(wp, run_lib(wp, out_fill=float("nan")), label="compact prefill grid, prefill steps only")
