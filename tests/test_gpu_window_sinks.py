@@ -136,3 +136,42 @@ def test_prefill_4x8192_window4096_sinks_every_row():
     sk = _bench_sinks(w.num_q_heads)
     got = run_lib(w, window=4096, sinks=sk, out_fill=float("nan"))
     check_every_row(w, got, window=4096, sinks=sk, label="4x8192 window 4096 sinks every row")
+
+
+def _takes_balanced_launch(w, window):
+    """Whether the call's plan runs its 16-row decode tiles as the balanced
+    launch: only that plan's workspace ends with (B + 4 U) * t * Hq * (D + 2)
+    float32 partial rows (U = ceil(2 CUs / Hkv) workgroups per KV head, t
+    token slots) and two ints per sequence after the split partials."""
+    import ctypes
+    from paged_kv_attention_amd import _lib as L
+    from gpu_util import to_dev
+    t = to_dev(w)
+    d = pa.make_dims(t["q"], t["k_pool"], t["block_tables"], max_query_len=w.max_query_len)
+    opts = L.PaAttnOpts(int(window), 0, None, None, 0, 0)
+    ws = int(L.load_library().pa_workspace_size_opts(ctypes.byref(d), L._dtype_code(w.dtype), ctypes.byref(opts)))
+    B, Hq, D, Hkv = len(w.context_lens), w.q.shape[1], w.q.shape[2], w.k_pool.shape[2]
+    U = -(-2 * pa.device_cu_count() // Hkv)
+    row = Hq * (D + 2) * 4
+    for tok in range(1, 17):
+        for k in range(1, 65):
+            split = (k * B * tok * row + 255) // 256 * 256
+            if ws == split + (B + 4 * U) * tok * row + B * 8:
+                return True
+    return False
+
+
+@pytest.mark.parametrize("window", [0, 11000])
+def test_bf16_mixed_batch_balanced_decodes_window_sinks(window):
+    # long decodes beside a prefill chunk and a verification step: one
+    # launch of all tiles with the decode class as the balanced launch (its
+    # splits would hold 2,048 keys or more), with and without a window that
+    # cuts the first thousands of keys of every long context, and sinks
+    lens = [12000, 14000, 16000, 13000, 15500, 12500, 1280, 2048, 100, 16000, 12345, 14800, 13333, 15001, 12002, 57]
+    qlens = [1, 1, 1, 1, 1, 1, 256, 5, 1, 1, 1, 1, 1, 1, 1, 1]
+    w = make_custom(seed=541, context_lens=lens, query_lens=qlens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                    page_size=64, dtype=torch.bfloat16)
+    assert _takes_balanced_launch(w, window), "batch no longer takes the balanced decode launch"
+    sk = _sinks(32, 9)
+    got = run_lib(w, window=window, sinks=sk, out_fill=float("nan"))
+    check(w, got, window=window, sinks=sk, label=f"mixed balanced window {window}")
