@@ -277,7 +277,8 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
 // This is the log-sum-exp merge of page "32. Production attention kernels"
 // (Long contexts: split the keys) written for unnormalised partials, as in
 // page "Attention and KV Cache" (Split-KV decode, Combine).
-// One 256-thread workgroup per row: the threads form 256 / (D/4) groups,
+// A 256-thread workgroup merges one row at a time (the rows of a query head
+// and sequence, every COMB_TSLOTS-th token): the threads form 256 / (D/4) groups,
 // group k takes splits k, k + groups, ... (each thread 4 dims), and the
 // first four splits of every group arrive together with their (m, l) pairs,
 // so a row with up to 4 * groups splits costs one memory latency.  The
@@ -287,13 +288,12 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2;
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
+__device__ __attribute__((always_inline)) void combine_row(const AttnParams& p, const int h, const int t, const int b) {
   constexpr int CPR = D / 4;                     // threads per partial row (4 dims each)
   constexpr int NGR = 256 / CPR;                 // split groups
   constexpr int BATCH = 4 * NGR;                 // splits whose loads are in flight at once
   __shared__ float red[NGR][D + 4];
   __shared__ float red_m[NGR], red_l[NGR];
-  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int grp = threadIdx.x / CPR, c4 = threadIdx.x % CPR;
   // the sequence's token range and, after a balanced launch, its partial
   // slots are requested together
@@ -401,9 +401,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
   }
 }
 
+// Grid: (query head, token slot, sequence) with at most COMB_TSLOTS token
+// slots; slot y takes the sequence's tokens y, y + COMB_TSLOTS, ...  A grid
+// with a slot for every token of the longest step idles most of its
+// workgroups beside one-token steps (a mixed batch with a 16-token bound:
+// 16,384 workgroups for 1,120 rows; 118.4-119.1 -> 116.5-118.0 us with four
+// slots, 119.8-121.0 us with one, where a verification step's rows run in
+// turn).
+constexpr int COMB_TSLOTS = 4;
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
+  const int n = p.query_start_loc[blockIdx.z + 1] - p.query_start_loc[blockIdx.z];
+  if (n > p.comb_max_n) return;
+  for (int t = blockIdx.y; t < n; t += gridDim.y) combine_row<D, BF16>(p, blockIdx.x, t, blockIdx.z);
+}
+
 template <int D>
 static hipError_t launch_combine_t(const AttnParams& p, bool bf16, hipStream_t st) {
-  dim3 grid(p.num_q_heads, p.comb_tokens, p.num_seqs);
+  dim3 grid(p.num_q_heads, p.comb_tokens < COMB_TSLOTS ? p.comb_tokens : COMB_TSLOTS, p.num_seqs);
   if (bf16)
     hipLaunchKernelGGL((combine_kernel<D, true>), grid, dim3(256), 0, st, p);
   else
