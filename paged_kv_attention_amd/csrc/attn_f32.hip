@@ -280,8 +280,8 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t st) {
 // A 256-thread workgroup merges one row at a time (the rows of a query head
 // and sequence, every COMB_TSLOTS-th token): the threads form 256 / (D/4) groups,
 // group k takes splits k, k + groups, ... (each thread 4 dims), and the
-// first four splits of every group arrive together with their (m, l) pairs,
-// so a row with up to 4 * groups splits costs one memory latency.  The
+// first eight splits of every group arrive together with their (m, l) pairs,
+// so a row with up to 8 * groups splits costs one memory latency.  The
 // groups' sums are added in LDS in group order, so the result does not
 // depend on scheduling.
 // ---------------------------------------------------------------------------
@@ -291,7 +291,8 @@ template <int D, bool BF16>
 __device__ __attribute__((always_inline)) void combine_row(const AttnParams& p, const int h, const int t, const int b) {
   constexpr int CPR = D / 4;                     // threads per partial row (4 dims each)
   constexpr int NGR = 256 / CPR;                 // split groups
-  constexpr int BATCH = 4 * NGR;                 // splits whose loads are in flight at once
+  constexpr int PB = 8;                          // splits of a group per batch
+  constexpr int BATCH = PB * NGR;                // splits whose loads are in flight at once
   __shared__ float red[NGR][D + 4];
   __shared__ float red_m[NGR], red_l[NGR];
   const int grp = threadIdx.x / CPR, c4 = threadIdx.x % CPR;
@@ -329,9 +330,9 @@ __device__ __attribute__((always_inline)) void combine_row(const AttnParams& p, 
   // (m, l) pairs and partial rows are loaded at once and kept, so a row with
   // up to BATCH splits costs one memory latency.  Padding entries are
   // (-inf, 0) and leave every sum bit for bit unchanged.
-  auto load = [&](int s, f32x2 (&ml)[4], f32x4 (&av)[4]) {
+  auto load = [&](int s, f32x2 (&ml)[PB], f32x4 (&av)[PB]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PB; ++j) {
       const int sj = s + j * NGR;
       if (sj < S) {
         const int64_t ri = (s_base + sj) * NH + row;
@@ -343,18 +344,18 @@ __device__ __attribute__((always_inline)) void combine_row(const AttnParams& p, 
       }
     }
   };
-  f32x2 ml0[4];
-  f32x4 av0[4];
+  f32x2 ml0[PB];
+  f32x4 av0[PB];
   load(grp, ml0, av0);
   float M = kNegInf;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) M = fmaxf(M, ml0[j][0]);
+  for (int j = 0; j < PB; ++j) M = fmaxf(M, ml0[j][0]);
   for (int s = grp + BATCH; s < S; s += BATCH) {
-    float m[4];
+    float m[PB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = s + j * NGR < S ? ml_p[((s_base + s + j * NGR) * NH + row) * 2] : kNegInf;
+    for (int j = 0; j < PB; ++j) m[j] = s + j * NGR < S ? ml_p[((s_base + s + j * NGR) * NH + row) * 2] : kNegInf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) M = fmaxf(M, m[j]);
+    for (int j = 0; j < PB; ++j) M = fmaxf(M, m[j]);
   }
   if (c4 == 0) red_m[grp] = M;
   __syncthreads();
@@ -364,17 +365,17 @@ __device__ __attribute__((always_inline)) void combine_row(const AttnParams& p, 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < PB; ++j) {
     const float w = fast_exp2(ml0[j][0] - Ms);
     l = fmaf(w, ml0[j][1], l);
     acc += w * av0[j];
   }
   for (int s = grp + BATCH; s < S; s += BATCH) {
-    f32x2 ml[4];
-    f32x4 av[4];
+    f32x2 ml[PB];
+    f32x4 av[PB];
     load(s, ml, av);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PB; ++j) {
       const float w = fast_exp2(ml[j][0] - Ms);
       l = fmaf(w, ml[j][1], l);
       acc += w * av[j];
