@@ -48,11 +48,11 @@ def test_fp32_mixed_batch_head_sizes(D):
     check(w, run_lib(w, num_splits=3), label=f"fp32 mixed D={D} S=3")
 
 
-@pytest.mark.parametrize("D,splits", [(64, 70), (128, 40), (256, 19)])
+@pytest.mark.parametrize("D,splits", [(64, 256), (128, 86), (256, 43)])
 def test_combine_second_pass_head_sizes(D, splits):
-    # more splits than the combine holds in registers per pass (64 at 64
-    # dims, 32 at 128, 16 at 256), float32 and bf16
-    lens = [2048, 1, 700, 1500]
+    # more splits than the combine holds in registers per pass (128 at 64
+    # dims, 64 at 128, 32 at 256), float32 and bf16; 256 pages of 16 keys
+    lens = [4096, 1, 700, 1500]
     for dtype in (torch.float32, torch.bfloat16):
         w = poison_unused(_custom(90 + D, lens, [1] * 4, Hq=8, Hkv=2, D=D, ps=16, dtype=dtype))
         check(w, run_lib(w, num_splits=splits), label=f"{dtype} D={D} S={splits}")
@@ -68,8 +68,8 @@ def test_fp32_mha_and_group3_not_causal():
 # ---------------------------------------------------------------- bf16 decode / verify
 # 11 and 19 splits: the cascade fold reads splits in groups of 8, so these
 # cover whole groups followed by a partial one; 33 and 64: the combine's
-# groups of threads hold their first 32 splits (128-dim heads) at once and
-# read the rest in a second pass
+# groups of threads hold up to 64 splits (128-dim heads) at once, partly and
+# wholly filled (its second pass: test_combine_second_pass_head_sizes)
 @pytest.mark.parametrize("splits", [0, 1, 3, 8, 11, 19, 33, 64])
 def test_bf16_decode_ragged(splits):
     lens = [1, 2, 63, 64, 65, 700, 2048, 4096, 33, 129]
